@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the fused NHWC int8 convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one fconv_plan_run of the whole layer (implicit-GEMM conv with the
+fused scale / side-input / bias / ReLU / requantise epilogue) over the full
+synthetic batch, inputs already resident in HBM, filter packed once per plan
+(as inference with fixed weights does).  W untimed steps, then exactly K
+timed steps bracketed by torch.cuda.synchronize(); prints ONE JSON line.
+
+value  = 2*N*Ho*Wo*K*R*S*C * K_steps / wall seconds, in TOPS.
+roofline: the conv kernel's algorithmic bytes (x + filter + side + y + bias,
+each once) per launch / its average launch duration from HIP events recorded
+on the launch stream around the timed region, against 8 TB/s HBM.
+cpu_baseline: the CPU oracle (direct loops + epilogue) timed on the host
+cores on the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused int8 conv TOPS (2·N·Ho·Wo·K·R·S·C/t) and % of MFMA peak, 1 GPU"
+PEAK_HBM_GBS = 8000.0
+PEAK_TOPS = {"int8": 5000.0, "bf16": 2500.0, "fp32": 157.3}  # dense MFMA
+KERNEL_SOURCES = [os.path.join(ROOT, "convolution_implicit_gemm_nhwc_amd", "csrc", f)
+                  for f in ("conv.hip", "plan.cpp", "plan.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(L) -> int:
+    """Each tensor once: x, filter, side input, y, per-channel vectors."""
+    esize = {"int8": 1, "bf16": 2, "fp32": 4}[L.dtype]
+    x = L.N * L.H * L.W * L.C * esize
+    w = L.R * L.S * L.C * L.K * esize
+    y = L.N * L.Ho * L.Wo * L.K * esize
+    side = L.N * L.Ho * L.Wo * L.K if L.has_side else 0
+    nvec = 1 + (4 if L.dtype != "int8" and 4 in L.ops else 0)
+    return x + w + y + side + 4 * L.K * nvec
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel") != kernel or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(L, inp, seconds: float):
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        acc = oracle.conv_acc(inp.x, inp.w, L.stride, L.padding)
+        y = oracle.epilogue_i8(acc, L.conv_input_scale, inp.bias, inp.side,
+                               L.side_input_scale, L.relu)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return y, dict(value=round(L.ops_count() * reps / dt / 1e12, 6), unit="TOPS",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample="full %s batch (N=%d), %d repetition(s) in %.1f s: direct "
+                          "7-loop conv + int8 epilogue, OpenMP over (n, ho)"
+                          % (L.name, L.N, reps, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="resnet_3x3_int8")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the fused convolution is batch-parallel "
+              "with no cross-GPU exchange, and this build runs on a single MI355X. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import convolution_implicit_gemm_nhwc_amd as fc
+    import workloads as wl
+
+    L = wl.LAYERS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = wl.make_inputs(L)
+    names = {wl.OP_SCALE: "scale", wl.OP_SIDE: "side", wl.OP_BIAS: "bias", wl.OP_BN: "bn",
+             wl.OP_RELU: "relu"}
+    plan = fc.Plan(L.N, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
+                   ops=[names[o] for o in L.ops])
+
+    def put(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, w, bias, side = put(inp.x), put(inp.w), put(inp.bias), put(inp.side)
+    bn = None
+    if inp.bn is not None:
+        bn = {k: put(np.asarray(inp.bn[k], np.float32)) for k in ("gamma", "beta", "mean", "var")}
+        bn["eps"] = float(inp.bn["eps"])
+    tdt = {"int8": torch.int8, "bf16": torch.bfloat16, "fp32": torch.float32}[L.dtype]
+    y = torch.empty(plan.out_shape, dtype=tdt, device=dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    plan.pack_filter(w, ws, stream)
+    run_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
+                              conv_input_scale=L.conv_input_scale,
+                              side_input_scale=L.side_input_scale, bn=bn, prepacked=True)
+    full_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
+                               conv_input_scale=L.conv_input_scale,
+                               side_input_scale=L.side_input_scale, bn=bn, prepacked=False)
+    h = stream.cuda_stream
+
+    def step(a=run_args):
+        st = plan.run_args(a, h)
+        if st != 0:
+            raise fc.FconvError(st, "fconv_plan_run")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    y_gpu = y.cpu()
+
+    # End to end including the per-call filter repack (not the headline).
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step(full_args)
+    torch.cuda.synchronize()
+    wall_full = time.perf_counter() - t2
+
+    ops = L.ops_count()
+    value = ops * args.steps / wall / 1e12
+    alg_bytes = algorithmic_bytes(L)
+    traffic = measured_traffic(L.name, plan.kernel_name)
+    # Bound: the roofline the layer meets first (ridge = peak ops / peak bytes).
+    ridge = PEAK_TOPS[L.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ops / alg_bytes <= ridge:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (kernel_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": ops / (kernel_ms * 1e-3) / 1e12,
+                "peak": PEAK_TOPS[L.dtype], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["achieved"] = round(roof["achieved"], 2)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"int8": "int8 (int32 accumulate)", "bf16": "bf16 (fp32 accumulate)",
+                  "fp32": "fp32"}[L.dtype],
+        "data": "synthetic",
+        "config": {"workload": L.name, "layer": L.description, "N": L.N, "H": L.H, "W": L.W,
+                   "C": L.C, "K": L.K, "R": L.R, "S": L.S, "stride": L.stride,
+                   "padding": L.padding, "filter": "prepacked once per plan",
+                   "kernel": plan.kernel_name},
+        "pct_of_mfma_peak": round(100.0 * value / PEAK_TOPS[L.dtype], 3),
+        "tops_from_kernel_time": round(ops / (kernel_ms * 1e-3) / 1e12, 4),
+        "tops_with_filter_repack_each_step": round(ops * args.steps / wall_full / 1e12, 4),
+        "roofline": dict(roof, traffic=traffic, kernel=plan.kernel_name,
+                         kernel_avg_us=round(kernel_ms * 1e3, 3),
+                         algorithmic_bytes_per_launch=alg_bytes),
+    }
+    if not args.no_cpu_baseline and L.dtype == "int8":
+        y_ref, cb = cpu_baseline(L, inp, args.cpu_seconds)
+        cb["sample_matches_gpu"] = bool(np.array_equal(y_ref, y_gpu.numpy()))
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+"""Fused NHWC implicit-GEMM convolution for AMD MI355X (gfx950).
+
+Python binding over the C ABI of ``include/fconv.h`` (``libfconv.so``).  It
+only marshals arguments: every step of the convolution and its epilogue runs
+in the library's HIP kernels.  Tensors are torch tensors on the GPU (torch
+provides device memory and streams) or raw device addresses given as ints.
+
+    plan = Plan(N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="int8",
+                ops=("scale", "side", "bias", "relu"))
+    y = plan(x, w, bias=b, side=s, conv_input_scale=2**-11, side_input_scale=0.25)
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+
+__all__ = ["Plan", "FconvError", "DTYPES", "OPS"]
+
+DTYPES = {"int8": _abi.FCONV_INT8, "bf16": _abi.FCONV_BF16, "fp32": _abi.FCONV_FP32}
+OPS = {"scale": _abi.OP_SCALE, "side": _abi.OP_SIDE, "bias": _abi.OP_BIAS,
+       "bn": _abi.OP_BN, "relu": _abi.OP_RELU}
+PADDINGS = {"SAME": _abi.FCONV_PAD_SAME, "VALID": _abi.FCONV_PAD_VALID}
+
+
+class FconvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _abi.lib().fconv_status_string(status).decode()
+        super().__init__("%s: %s (status %d)" % (what, msg, status))
+
+
+def _check(status: int, what: str):
+    if status != _abi.FCONV_OK:
+        raise FconvError(status, what)
+
+
+def _addr(t):
+    """Device address of a torch GPU tensor (or an int address / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU (got %s)" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """A resolved fused-conv plan (geometry, dtype, ordered epilogue ops)."""
+
+    def __init__(self, N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="int8",
+                 ops=("scale", "bias")):
+        sh, sw = (stride, stride) if isinstance(stride, int) else stride
+        d = _abi.FconvDesc()
+        d.N, d.H, d.W, d.C, d.K, d.R, d.S = N, H, W, C, K, R, S
+        d.stride_h, d.stride_w = sh, sw
+        d.padding = PADDINGS[padding.upper()] if isinstance(padding, str) else padding
+        d.dtype = DTYPES[dtype] if isinstance(dtype, str) else dtype
+        codes = [OPS[o] if isinstance(o, str) else int(o) for o in ops]
+        if len(codes) > _abi.FCONV_MAX_OPS:
+            raise ValueError("too many ops")
+        d.n_ops = len(codes)
+        for i, c in enumerate(codes):
+            d.ops[i] = c
+        d.flags = 0
+        self.desc = d
+        self.dtype = dtype
+        self._h = ctypes.c_void_p()
+        _check(_abi.lib().fconv_plan_create(ctypes.byref(d), ctypes.byref(self._h)),
+               "fconv_plan_create")
+        ho, wo = ctypes.c_int32(), ctypes.c_int32()
+        pads = (ctypes.c_int32 * 4)()
+        _check(_abi.lib().fconv_plan_output_dims(self._h, ctypes.byref(ho),
+                                                 ctypes.byref(wo), pads),
+               "fconv_plan_output_dims")
+        self.Ho, self.Wo = ho.value, wo.value
+        self.pads = tuple(pads)
+        nbytes = ctypes.c_size_t()
+        _check(_abi.lib().fconv_plan_workspace_size(self._h, ctypes.byref(nbytes)),
+               "fconv_plan_workspace_size")
+        self.workspace_bytes = nbytes.value
+        self.kernel_name = _abi.lib().fconv_plan_kernel_name(self._h).decode()
+        self.out_shape = (N, self.Ho, self.Wo, K)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _abi.lib().fconv_plan_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def pack_filter(self, w, workspace, stream=None):
+        _check(_abi.lib().fconv_plan_pack_filter(
+            self._h, _stream_handle(stream), _addr(w), _addr(workspace),
+            self.workspace_bytes if not isinstance(workspace, int) else self.workspace_bytes),
+            "fconv_plan_pack_filter")
+
+    def make_args(self, x, w, y, workspace, bias=None, side=None, conv_input_scale=1.0,
+                  side_input_scale=0.0, bn=None, prepacked=False, workspace_bytes=None):
+        a = _abi.FconvArgs()
+        a.x, a.w, a.y = _addr(x), _addr(w), _addr(y)
+        a.workspace = _addr(workspace)
+        if workspace_bytes is None:
+            workspace_bytes = (workspace.numel() * workspace.element_size()
+                               if hasattr(workspace, "numel") else self.workspace_bytes)
+        a.workspace_bytes = workspace_bytes
+        a.bias, a.side = _addr(bias), _addr(side)
+        a.conv_input_scale = conv_input_scale
+        a.side_input_scale = side_input_scale
+        if bn is not None:
+            a.bn_gamma, a.bn_beta = _addr(bn["gamma"]), _addr(bn["beta"])
+            a.bn_mean, a.bn_var = _addr(bn["mean"]), _addr(bn["var"])
+            a.bn_eps = bn["eps"]
+        a.flags = _abi.FCONV_RUN_FILTER_PREPACKED if prepacked else 0
+        return a
+
+    def run_args(self, args, stream=None) -> int:
+        """Enqueue with a prepared FconvArgs; returns the raw status."""
+        return _abi.lib().fconv_plan_run(self._h, _stream_handle(stream), ctypes.byref(args))
+
+    def run(self, x, w, y, workspace, stream=None, **kw):
+        _check(self.run_args(self.make_args(x, w, y, workspace, **kw), stream),
+               "fconv_plan_run")
+        return y
+
+    def __call__(self, x, w, stream=None, **kw):
+        """Allocate y and the workspace with torch, run, return y."""
+        import torch
+        tdt = {"int8": torch.int8, "bf16": torch.bfloat16, "fp32": torch.float32}[self.dtype]
+        y = torch.empty(self.out_shape, dtype=tdt, device=x.device)
+        ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=x.device)
+        return self.run(x, w, y, ws, stream=stream, **kw)

@@ -1,0 +1,249 @@
+// Plan creation and argument validation (host only, no HIP calls).
+//
+// The split between a plan (geometry + ordered operators, resolved once) and
+// per-run arguments follows MIOpen "Using the fusion API" (sections "Creating
+// a fusion plan", "Compiling the fusion plan", "Setting runtime arguments").
+// The argument checks mirror the ones TensorFlow conv_ops_fused_int8.cc makes
+// before its fused int8 conv (LaunchFusedConv2DOpCpuInt8Helper: no groups,
+// NHWC, dilation 1, BiasAdd with or without Relu) but report status codes
+// instead of aborting.
+#include <limits.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "plan.h"
+
+namespace {
+
+using namespace fconv;
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Output size and padding.  SAME: TensorFlow conv_ops_fused_int8.cc,
+// LaunchFusedConv2DOpGpuInt8Helper -- the total padding is
+// max(0, (out-1)*stride + filter - in), half of it (rounded down) before and
+// the rest after; the output size is ceil(in / stride).  VALID: no padding.
+bool resolve_axis(int32_t in, int32_t f, int32_t stride, bool same, int32_t* out,
+                  int32_t* before, int32_t* after) {
+  if (same) {
+    int64_t o = (static_cast<int64_t>(in) + stride - 1) / stride;
+    int64_t total = (o - 1) * stride + f - in;
+    if (total < 0) total = 0;
+    *out = static_cast<int32_t>(o);
+    *before = static_cast<int32_t>(total / 2);
+    *after = static_cast<int32_t>(total - total / 2);
+    return true;
+  }
+  if (in < f) return false;
+  *out = (in - f) / stride + 1;
+  *before = *after = 0;
+  return true;
+}
+
+// Accepted operator sequences; see the fconv_op comment in fconv.h.
+fconv_status parse_ops(fconv_plan_s* p) {
+  const fconv_desc& d = p->d;
+  if (d.n_ops < 0 || d.n_ops > FCONV_MAX_OPS) return FCONV_ERR_INVALID_ARG;
+  p->op_scale = p->op_side = p->op_bias = p->op_bn = p->op_relu = false;
+  int i = 0;
+  auto next_is = [&](int32_t op) {
+    if (i < d.n_ops && d.ops[i] == op) {
+      ++i;
+      return true;
+    }
+    return false;
+  };
+  if (d.dtype == FCONV_INT8) {
+    // TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel: scale,
+    // side input, bias, then BiasAdd or BiasAdd+Relu.
+    p->op_scale = next_is(FCONV_OP_SCALE);
+    p->op_side = next_is(FCONV_OP_SIDE);
+    p->op_bias = next_is(FCONV_OP_BIAS);
+    p->op_relu = next_is(FCONV_OP_RELU);
+    if (!p->op_scale || !p->op_bias) return FCONV_ERR_UNSUPPORTED;
+  } else {
+    // MIOpen supported fusions: conv -> bias -> batch norm -> activation.
+    p->op_bias = next_is(FCONV_OP_BIAS);
+    p->op_bn = next_is(FCONV_OP_BN);
+    p->op_relu = next_is(FCONV_OP_RELU);
+  }
+  if (i != d.n_ops) return FCONV_ERR_UNSUPPORTED;
+  return FCONV_OK;
+}
+
+const char* general_kernel_name(int32_t dtype) {
+  switch (dtype) {
+    case FCONV_INT8: return "conv_general_i8";
+    case FCONV_BF16: return "conv_general_bf16";
+    default: return "conv_general_f32";
+  }
+}
+
+void choose_variant(fconv_plan_s* p) {
+  p->variant = kGeneral;
+  p->kernel_name = general_kernel_name(p->d.dtype);
+}
+
+bool aligned(const void* ptr, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+namespace fconv {
+
+fconv_status check_pack_args(const fconv_plan_s* p, const void* w,
+                             const void* workspace, size_t workspace_bytes) {
+  if (!p || !w) return FCONV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < p->ws_bytes) return FCONV_ERR_WORKSPACE;
+  if (!aligned(w, 16) || !aligned(workspace, 16)) return FCONV_ERR_MISALIGNED;
+  if (overlap(w, static_cast<size_t>(p->w_elems) * p->esize, workspace, p->ws_bytes))
+    return FCONV_ERR_INVALID_ARG;
+  return FCONV_OK;
+}
+
+fconv_status check_run_args(const fconv_plan_s* p, const fconv_args* a) {
+  if (!p || !a) return FCONV_ERR_INVALID_ARG;
+  if (a->flags & ~FCONV_RUN_FILTER_PREPACKED) return FCONV_ERR_UNSUPPORTED;
+  const bool prepacked = (a->flags & FCONV_RUN_FILTER_PREPACKED) != 0;
+  if (!a->x || !a->y) return FCONV_ERR_INVALID_ARG;
+  if (!prepacked && !a->w) return FCONV_ERR_INVALID_ARG;
+  if (p->op_bias && !a->bias) return FCONV_ERR_INVALID_ARG;
+  if (p->op_side && !a->side) return FCONV_ERR_INVALID_ARG;
+  if (p->op_bn && (!a->bn_gamma || !a->bn_beta || !a->bn_mean || !a->bn_var))
+    return FCONV_ERR_INVALID_ARG;
+  if (!a->workspace || a->workspace_bytes < p->ws_bytes) return FCONV_ERR_WORKSPACE;
+  if (!aligned(a->x, 16) || !aligned(a->y, 16) || !aligned(a->workspace, 16) ||
+      (!prepacked && !aligned(a->w, 16)) || (p->op_side && !aligned(a->side, 16)))
+    return FCONV_ERR_MISALIGNED;
+  const float* vecs[5] = {p->op_bias ? a->bias : nullptr,
+                          p->op_bn ? a->bn_gamma : nullptr,
+                          p->op_bn ? a->bn_beta : nullptr,
+                          p->op_bn ? a->bn_mean : nullptr,
+                          p->op_bn ? a->bn_var : nullptr};
+  for (const float* v : vecs)
+    if (v && !aligned(v, 4)) return FCONV_ERR_MISALIGNED;
+  // No in-place operation: y may not overlap anything the run reads, nor the
+  // workspace it writes.
+  const size_t yb = static_cast<size_t>(p->y_elems) * p->esize;
+  const size_t xb = static_cast<size_t>(p->x_elems) * p->esize;
+  const size_t wb = static_cast<size_t>(p->w_elems) * p->esize;
+  if (overlap(a->y, yb, a->x, xb) || overlap(a->y, yb, a->workspace, p->ws_bytes) ||
+      (!prepacked && overlap(a->y, yb, a->w, wb)) ||
+      (p->op_side && overlap(a->y, yb, a->side, static_cast<size_t>(p->y_elems))))
+    return FCONV_ERR_INVALID_ARG;
+  if (!prepacked && overlap(a->w, wb, a->workspace, p->ws_bytes))
+    return FCONV_ERR_INVALID_ARG;
+  return FCONV_OK;
+}
+
+}  // namespace fconv
+
+extern "C" {
+
+fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
+  if (!desc || !out) return FCONV_ERR_INVALID_ARG;
+  *out = nullptr;
+  const fconv_desc& d = *desc;
+  if (d.dtype != FCONV_INT8 && d.dtype != FCONV_BF16 && d.dtype != FCONV_FP32)
+    return FCONV_ERR_UNSUPPORTED;
+  if (d.padding != FCONV_PAD_SAME && d.padding != FCONV_PAD_VALID)
+    return FCONV_ERR_UNSUPPORTED;
+  if (d.flags != 0) return FCONV_ERR_UNSUPPORTED;
+  if (d.N < 0 || d.H < 1 || d.W < 1 || d.C < 1 || d.K < 1 || d.R < 1 || d.S < 1 ||
+      d.stride_h < 1 || d.stride_w < 1)
+    return FCONV_ERR_INVALID_ARG;
+
+  fconv_plan_s* p = new (std::nothrow) fconv_plan_s();
+  if (!p) return FCONV_ERR_INVALID_ARG;
+  p->d = d;
+  const bool same = d.padding == FCONV_PAD_SAME;
+  if (!resolve_axis(d.H, d.R, d.stride_h, same, &p->Ho, &p->pt, &p->pb) ||
+      !resolve_axis(d.W, d.S, d.stride_w, same, &p->Wo, &p->pl, &p->pr)) {
+    delete p;
+    return FCONV_ERR_INVALID_ARG;
+  }
+  fconv_status st = parse_ops(p);
+  if (st != FCONV_OK) {
+    delete p;
+    return st;
+  }
+  p->esize = d.dtype == FCONV_INT8 ? 1 : d.dtype == FCONV_BF16 ? 2 : 4;
+  p->chunk_elems = 16 / p->esize;
+  p->x_elems = static_cast<int64_t>(d.N) * d.H * d.W * d.C;
+  p->M = static_cast<int64_t>(d.N) * p->Ho * p->Wo;
+  p->y_elems = p->M * d.K;
+  p->w_elems = static_cast<int64_t>(d.R) * d.S * d.C * d.K;
+  const int64_t kg = static_cast<int64_t>(d.R) * d.S * d.C;
+  const int64_t kstep = 4 * p->chunk_elems;
+  const int64_t kgp = round_up(kg, kstep);
+  const int64_t kp = round_up(d.K, 64);
+  // Kernels index with 32-bit element offsets.
+  if (p->x_elems >= INT32_MAX || p->y_elems >= INT32_MAX || kp * kgp >= INT32_MAX ||
+      p->M >= INT32_MAX) {
+    delete p;
+    return FCONV_ERR_UNSUPPORTED;
+  }
+  p->Kg = static_cast<int32_t>(kg);
+  p->KgP = static_cast<int32_t>(kgp);
+  p->Kp = static_cast<int32_t>(kp);
+  p->ws_bytes = static_cast<size_t>(kp * kgp * p->esize);
+  if (d.C % kstep == 0)
+    p->load_mode = kLoadTap;
+  else if (d.C % p->chunk_elems == 0)
+    p->load_mode = kLoadChunk;
+  else
+    p->load_mode = kLoadElem;
+  choose_variant(p);
+  *out = p;
+  return FCONV_OK;
+}
+
+fconv_status fconv_plan_output_dims(fconv_plan p, int32_t* Ho, int32_t* Wo,
+                                    int32_t pads_tblr[4]) {
+  if (!p) return FCONV_ERR_INVALID_ARG;
+  if (Ho) *Ho = p->Ho;
+  if (Wo) *Wo = p->Wo;
+  if (pads_tblr) {
+    pads_tblr[0] = p->pt;
+    pads_tblr[1] = p->pb;
+    pads_tblr[2] = p->pl;
+    pads_tblr[3] = p->pr;
+  }
+  return FCONV_OK;
+}
+
+fconv_status fconv_plan_workspace_size(fconv_plan p, size_t* bytes) {
+  if (!p || !bytes) return FCONV_ERR_INVALID_ARG;
+  *bytes = p->ws_bytes;
+  return FCONV_OK;
+}
+
+fconv_status fconv_plan_destroy(fconv_plan p) {
+  delete p;
+  return FCONV_OK;
+}
+
+const char* fconv_plan_kernel_name(fconv_plan p) { return p ? p->kernel_name : nullptr; }
+
+const char* fconv_status_string(fconv_status s) {
+  switch (s) {
+    case FCONV_OK: return "ok";
+    case FCONV_ERR_INVALID_ARG: return "invalid argument";
+    case FCONV_ERR_UNSUPPORTED: return "unsupported";
+    case FCONV_ERR_WORKSPACE: return "workspace missing or too small";
+    case FCONV_ERR_MISALIGNED: return "misaligned pointer";
+    case FCONV_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Host-side plan object shared by plan.cpp (validation, geometry, variant
+// choice; no HIP) and the kernel launchers in conv.hip.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fconv.h"
+
+namespace fconv {
+
+// Kernel families.  Every plan can fall back to kGeneral; the others are
+// shape-specialised tilings chosen by choose_variant() in plan.cpp.
+enum Variant : int32_t {
+  kGeneral = 0,  // any shape: direct-from-global implicit GEMM, 64x64 tile
+};
+
+// How the implicit-GEMM A operand (im2col row) is gathered, per 16-byte
+// chunk of the reduction dimension (r, s, c):
+//   kLoadTap:   C is a multiple of one k-step, so a whole k-step sits in one
+//               filter tap and the tap loop is uniform across the wave;
+//   kLoadChunk: C is a multiple of a 16-byte chunk; one predicated 128-bit
+//               load per chunk, tap decoded per lane;
+//   kLoadElem:  anything else; element-wise predicated loads.
+enum LoadMode : int32_t { kLoadTap = 0, kLoadChunk = 1, kLoadElem = 2 };
+
+}  // namespace fconv
+
+struct fconv_plan_s {
+  fconv_desc d;
+  int32_t Ho, Wo, pt, pb, pl, pr;
+  int32_t esize;       // bytes per x/w/y element
+  int32_t chunk_elems; // elements per 16-byte chunk (16 int8, 8 bf16, 4 fp32)
+  bool op_scale, op_side, op_bias, op_bn, op_relu;
+  int64_t M;      // N * Ho * Wo, rows of the implicit GEMM
+  int32_t Kg;     // R * S * C, reduction length
+  int32_t KgP;    // Kg rounded up to whole k-steps (4 chunks)
+  int32_t Kp;     // K rounded up to a multiple of 64 (packed filter rows)
+  int32_t load_mode;
+  int32_t variant;
+  size_t ws_bytes;  // packed filter: Kp * KgP * esize
+  int64_t x_elems, y_elems, w_elems;
+  const char* kernel_name;
+};
+
+namespace fconv {
+// Argument checks of fconv_plan_run / fconv_plan_pack_filter that need no
+// device: pointers, alignment, workspace size, aliasing.  Implemented in
+// plan.cpp.
+fconv_status check_run_args(const fconv_plan_s* p, const fconv_args* a);
+fconv_status check_pack_args(const fconv_plan_s* p, const void* w,
+                             const void* workspace, size_t workspace_bytes);
+}  // namespace fconv

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+int8 outputs must be bit-exact; bf16 and fp32 must be within the normwise
+tolerances in gpu_helpers.TOL of the float64 oracle fed the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import (TOL, device, float_error, make_plan, oracle_out, run_gpu, say,
+                         to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_case(L, N=None):
+    inp = wl.make_inputs(L, N=N)
+    n = inp.x.shape[0]
+    plan = make_plan(n, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype, L.ops)
+    return inp, plan
+
+
+def _check_layer(L, N=None, prepacked=False):
+    inp, plan = _layer_case(L, N)
+    say("layer %s N=%d kernel=%s prepacked=%s" % (L.name, inp.x.shape[0], plan.kernel_name,
+                                                   prepacked))
+    ws = None
+    if prepacked:
+        dev = device()
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        plan.pack_filter(to_dev(inp.w, dev), ws)
+    y, guards = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, inp.side,
+                        L.conv_input_scale, L.side_input_scale, inp.bn, prepacked_ws=ws,
+                        guard=256)
+    assert guards, "write outside y"
+    r = oracle_out(L.dtype, inp.x, inp.w, L.stride, L.padding, inp.bias, inp.side,
+                   L.conv_input_scale, L.side_input_scale, L.relu, inp.bn,
+                   use_bias=wl.OP_BIAS in L.ops)
+    if L.dtype == "int8":
+        bad = np.count_nonzero(y != r)
+        assert bad == 0, "%d of %d int8 outputs differ" % (bad, r.size)
+    else:
+        e = float_error(y, r)
+        say("  normwise error %.3e (tolerance %.0e)" % (e, TOL[L.dtype]))
+        assert e <= TOL[L.dtype]
+    return y
+
+
+@pytest.mark.parametrize("name", list(wl.LAYERS))
+def test_workload_full_size(name):
+    _check_layer(wl.LAYERS[name])
+
+
+@pytest.mark.parametrize("name", ["resnet_3x3_int8", "resnet_1x1_int8", "resnet_3x3s2_int8",
+                                  "resnet_3x3_bf16_bn"])
+def test_workload_prepacked_filter(name):
+    """The launch configuration the benchmark times: filter packed once."""
+    _check_layer(wl.LAYERS[name], prepacked=True)
+
+
+def _random_case(rng, dtype):
+    p = wl.random_small_case(rng)
+    N, H, W, C, K, R, S, st, pad = (p[k] for k in ("N", "H", "W", "C", "K", "R", "S",
+                                                  "stride", "padding"))
+    Ho, Wo = oracle.geometry(H, W, R, S, st, st, pad == "SAME")[:2]
+    if dtype == "int8":
+        x = wl.draw_int8(rng, (N, H, W, C), -128, 127)
+        w = wl.draw_int8(rng, (R, S, C, K), -128, 127)
+        bias = rng.normal(0, 30, K).astype(np.float32)
+        use_side = rng.random() < 0.5
+        side = wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if use_side else None
+        relu = bool(rng.random() < 0.5)
+        cis = np.float32(rng.choice([2.0 ** -8, 0.0123, 1 / 3, 1.0, 2.0 ** -11]))
+        sis = np.float32(rng.choice([0.5, 0.377, 0.0, 1.0])) if use_side else np.float32(0)
+        ops = [wl.OP_SCALE] + ([wl.OP_SIDE] if use_side else []) + [wl.OP_BIAS] + (
+            [wl.OP_RELU] if relu else [])
+        return dict(shape=(N, H, W, C, K, R, S, st, pad), x=x, w=w, bias=bias, side=side,
+                    cis=cis, sis=sis, relu=relu, ops=ops, bn=None, use_bias=True)
+    sd = 1.0 / np.sqrt(R * S * C)
+    x = rng.normal(0, 1, (N, H, W, C)).astype(np.float32)
+    w = rng.normal(0, sd, (R, S, C, K)).astype(np.float32)
+    if dtype == "bf16":
+        x, w = wl.float_to_bf16_bits(x), wl.float_to_bf16_bits(w)
+    use_bias = bool(rng.random() < 0.7)
+    use_bn = bool(rng.random() < 0.6)
+    relu = bool(rng.random() < 0.5)
+    bias = rng.normal(0, 0.1, K).astype(np.float32)
+    bn = dict(mean=rng.normal(0, 0.1, K).astype(np.float32),
+              var=rng.uniform(0.5, 1.5, K).astype(np.float32),
+              gamma=rng.uniform(0.5, 1.5, K).astype(np.float32),
+              beta=rng.normal(0, 0.1, K).astype(np.float32), eps=1e-5) if use_bn else None
+    ops = ([wl.OP_BIAS] if use_bias else []) + ([wl.OP_BN] if use_bn else []) + (
+        [wl.OP_RELU] if relu else [])
+    return dict(shape=(N, H, W, C, K, R, S, st, pad), x=x, w=w, bias=bias, side=None,
+                cis=1.0, sis=0.0, relu=relu, ops=ops, bn=bn, use_bias=use_bias)
+
+
+def _run_case(c, dtype):
+    N, H, W, C, K, R, S, st, pad = c["shape"]
+    plan = make_plan(N, H, W, C, K, R, S, st, pad, dtype, c["ops"])
+    y, guards = run_gpu(plan, dtype, c["x"], c["w"], c["bias"], c["side"], c["cis"], c["sis"],
+                        c["bn"], guard=64)
+    r = oracle_out(dtype, c["x"], c["w"], st, pad, c["bias"], c["side"], c["cis"], c["sis"],
+                   c["relu"], c["bn"], c["use_bias"])
+    return y, r, guards, plan
+
+
+@pytest.mark.parametrize("dtype,count,seed", [("int8", 160, 100), ("bf16", 50, 200),
+                                              ("fp32", 50, 300)])
+def test_fuzz_small_shapes(dtype, count, seed):
+    """Random small layers: C, K not multiples of 16, filters 1-5, strides 1-3,
+    SAME/VALID, images smaller than the filter; several tiles and ragged tails."""
+    rng = np.random.default_rng(seed)
+    say("fuzz %s: %d cases" % (dtype, count))
+    for i in range(count):
+        c = _random_case(rng, dtype)
+        y, r, guards, plan = _run_case(c, dtype)
+        where = "case %d %s %s" % (i, c["shape"], plan.kernel_name)
+        assert guards, where
+        if dtype == "int8":
+            assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)
+        else:
+            tol = TOL[dtype] if dtype == "bf16" else 2e-6
+            assert float_error(y, r) <= tol, where
+
+
+@pytest.mark.parametrize("C,K,H,W,R,stride,pad", [
+    (64, 64, 9, 13, 3, 1, "SAME"), (128, 128, 11, 11, 3, 2, "SAME"),
+    (256, 64, 7, 9, 1, 1, "VALID"), (16, 32, 17, 5, 3, 1, "SAME"), (48, 80, 6, 6, 5, 2, "SAME"),
+    (64, 8, 4, 4, 3, 1, "VALID"), (256, 256, 5, 5, 3, 1, "SAME"), (32, 200, 3, 70, 2, 3, "SAME")])
+@pytest.mark.parametrize("dtype", ["int8", "bf16", "fp32"])
+def test_tile_shapes(C, K, H, W, R, stride, pad, dtype):
+    """Channel counts on and off the vector widths, several 64-channel blocks,
+    ragged pixel tails."""
+    rng = np.random.default_rng(C * 1000 + K)
+    Ho, Wo = oracle.geometry(H, W, R, R, stride, stride, pad == "SAME")[:2]
+    N = 3
+    if dtype == "int8":
+        x = wl.draw_int8(rng, (N, H, W, C), -128, 127)
+        w = wl.draw_int8(rng, (R, R, C, K), -128, 127)
+        side = wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127)
+        c = dict(shape=(N, H, W, C, K, R, R, stride, pad), x=x, w=w,
+                 bias=rng.normal(0, 50, K).astype(np.float32), side=side,
+                 cis=np.float32(2.0 ** -9), sis=np.float32(0.75), relu=False,
+                 ops=[wl.OP_SCALE, wl.OP_SIDE, wl.OP_BIAS], bn=None, use_bias=True)
+    else:
+        x = rng.normal(0, 1, (N, H, W, C)).astype(np.float32)
+        w = rng.normal(0, 1 / np.sqrt(R * R * C), (R, R, C, K)).astype(np.float32)
+        if dtype == "bf16":
+            x, w = wl.float_to_bf16_bits(x), wl.float_to_bf16_bits(w)
+        bn = dict(mean=rng.normal(0, .1, K).astype(np.float32),
+                  var=rng.uniform(.5, 1.5, K).astype(np.float32),
+                  gamma=rng.uniform(.5, 1.5, K).astype(np.float32),
+                  beta=rng.normal(0, .1, K).astype(np.float32), eps=1e-5)
+        c = dict(shape=(N, H, W, C, K, R, R, stride, pad), x=x, w=w,
+                 bias=rng.normal(0, .1, K).astype(np.float32), side=None, cis=1.0, sis=0.0,
+                 relu=True, ops=[wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], bn=bn, use_bias=True)
+    say("tile shape %s %s" % (dtype, c["shape"]))
+    y, r, guards, plan = _run_case(c, dtype)
+    assert guards
+    if dtype == "int8":
+        assert np.array_equal(y, r), "%d differ" % np.count_nonzero(y != r)
+    else:
+        assert float_error(y, r) <= (TOL["bf16"] if dtype == "bf16" else 2e-6)
+
+
+def test_crafted_fma_and_contraction_cases():
+    """T1 (side step must be one fused multiply-add) and T2 (scale and bias
+    must not be contracted), single-pixel 1x1 convolutions."""
+    for C, xv, wv, cis, side, sis, bias, exp in [
+            (2, 64, 64, 1024.0, 3, 0.1666666716337204, -8388608.0, 1),
+            (1, 5, 1, 838860.9375, None, 0.0, -4194304.0, 0)]:
+        x = np.full((1, 1, 1, C), xv, np.int8)
+        w = np.full((1, 1, C, 1), wv, np.int8)
+        s = None if side is None else np.full((1, 1, 1, 1), side, np.int8)
+        ops = [wl.OP_SCALE] + ([wl.OP_SIDE] if s is not None else []) + [wl.OP_BIAS]
+        plan = make_plan(1, 1, 1, C, 1, 1, 1, 1, "VALID", "int8", ops)
+        y, _ = run_gpu(plan, "int8", x, w, np.array([bias], np.float32), s, np.float32(cis),
+                       np.float32(sis))
+        assert int(y[0, 0, 0, 0]) == exp
+
+
+def test_tie_dense_round_half_even():
+    """scale 0.5, bias 0, no side: every odd accumulator is an exact tie."""
+    rng = np.random.default_rng(21)
+    x = wl.draw_int8(rng, (4, 12, 12, 64), -9, 9)
+    w = wl.draw_int8(rng, (3, 3, 64, 64), -9, 9)
+    plan = make_plan(4, 12, 12, 64, 64, 3, 3, 1, "SAME", "int8", [wl.OP_SCALE, wl.OP_BIAS])
+    bias = np.zeros(64, np.float32)
+    y, _ = run_gpu(plan, "int8", x, w, bias, None, 0.5)
+    acc = oracle.conv_acc(x, w, 1, "SAME")
+    assert np.mean(acc % 2 != 0) > 0.3
+    assert np.array_equal(y, np.clip(np.round(acc / 2.0), -128, 127).astype(np.int8))
+
+
+def test_zero_side_scale_skips_side():
+    rng = np.random.default_rng(22)
+    x = wl.draw_int8(rng, (2, 9, 9, 32))
+    w = wl.draw_int8(rng, (3, 3, 32, 32))
+    side = wl.draw_int8(rng, (2, 9, 9, 32))
+    bias = rng.normal(0, 20, 32).astype(np.float32)
+    plan = make_plan(2, 9, 9, 32, 32, 3, 3, 1, "SAME", "int8",
+                     [wl.OP_SCALE, wl.OP_SIDE, wl.OP_BIAS, wl.OP_RELU])
+    y, _ = run_gpu(plan, "int8", x, w, bias, side, 2.0 ** -10, 0.0)
+    r = oracle.fused_conv_i8(x, w, bias, 2.0 ** -10, None, 0.0, True, 1, "SAME")
+    assert np.array_equal(y, r)
+
+
+def test_run_twice_is_bit_identical():
+    L = wl.LAYERS["resnet_3x3_bf16_bn"]
+    inp, plan = _layer_case(L, N=2)
+    a, _ = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, None, bn=inp.bn)
+    b, _ = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, None, bn=inp.bn)
+    assert np.array_equal(a, b)
+
+
+def test_empty_batch_is_a_no_op():
+    dev = device()
+    plan = make_plan(0, 8, 8, 16, 16, 3, 3, 1, "SAME", "int8", [wl.OP_SCALE, wl.OP_BIAS])
+    x = torch.zeros(16, dtype=torch.int8, device=dev)
+    y = torch.full((16,), 7, dtype=torch.int8, device=dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    w = torch.zeros(3 * 3 * 16 * 16, dtype=torch.int8, device=dev)
+    b = torch.zeros(16, dtype=torch.float32, device=dev)
+    plan.run(x, w, y, ws, bias=b)
+    torch.cuda.synchronize()
+    assert (y.cpu() == 7).all()
+
+
+def test_pack_filter_then_prepacked_run_matches():
+    rng = np.random.default_rng(23)
+    dev = device()
+    for dtype in ("int8", "bf16", "fp32"):
+        C, K = 48, 72
+        plan = make_plan(2, 7, 7, C, K, 3, 3, 1, "SAME", dtype,
+                         [wl.OP_SCALE, wl.OP_BIAS] if dtype == "int8" else [wl.OP_BIAS])
+        if dtype == "int8":
+            x, w = wl.draw_int8(rng, (2, 7, 7, C)), wl.draw_int8(rng, (3, 3, C, K))
+        else:
+            x = rng.normal(0, 1, (2, 7, 7, C)).astype(np.float32)
+            w = rng.normal(0, .1, (3, 3, C, K)).astype(np.float32)
+            if dtype == "bf16":
+                x, w = wl.float_to_bf16_bits(x), wl.float_to_bf16_bits(w)
+        bias = rng.normal(0, 1, K).astype(np.float32)
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        plan.pack_filter(to_dev(w, dev), ws)
+        a, _ = run_gpu(plan, dtype, x, w, bias, None, 2.0 ** -8, prepacked_ws=ws)
+        b, _ = run_gpu(plan, dtype, x, w, bias, None, 2.0 ** -8)
+        assert np.array_equal(a, b), dtype
