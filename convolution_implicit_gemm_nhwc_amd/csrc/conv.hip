@@ -109,14 +109,21 @@ struct ConvArgs {
   float cis, sis, bn_eps;
   int32_t N, H, W, C, K, R, S, sh, sw, pt, pl, Ho, Wo;
   int32_t M, Kg, KgP;
+  int32_t wrow_bytes;  // packed filter row stride: KgP * elem + 16 (zero pad)
+  uint32_t x_bytes, y_bytes, side_bytes;  // buffer-descriptor extents
+  uint32_t wp_bytes;                      // packed filter extent
+  int32_t tiles;                          // ceil(M / 16) pixel tiles
+  // m / Wo and q / Ho by multiply-high: q = (umulhi(n, mul) + (add ? n : 0)) >> shift
+  uint32_t wo_mul, wo_add, wo_shift, ho_mul, ho_add, ho_shift;
   int32_t use_side, use_bias, use_bn, relu;
 };
 
 // ------------------------------------------------------------ filter repack
 
-// HWIO [R][S][C][K] (= [Kg][K]) -> packed [Kp][KgP], rows in the permuted
-// channel order above, reduction contiguous, zero-filled past K and Kg.
-// One thread per 16-byte chunk of the packed filter.
+// HWIO [R][S][C][K] (= [Kg][K]) -> packed [Kp] rows of KgP elements plus a
+// 16-byte zero pad (row stride wrow_bytes, an odd multiple of 16 bytes), rows
+// in the permuted channel order above, reduction contiguous, zero-filled past
+// K and Kg.  One thread per 16-byte chunk of the packed filter.
 template <int DT>
 __global__ __launch_bounds__(256) void pack_filter_kernel(const void* __restrict__ w_,
                                                           void* __restrict__ wp_,
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(256) void pack_filter_kernel(const void* __restrict
   constexpr int E = Dt<DT>::kChunk;
   const T* w = static_cast<const T*>(w_);
   T* wp = static_cast<T*>(wp_);
-  const int chunks_per_row = KgP / E;
+  const int chunks_per_row = KgP / E + 1;  // + the pad chunk
   const int64_t id = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (id >= static_cast<int64_t>(Kp) * chunks_per_row) return;
   const int p = static_cast<int>(id / chunks_per_row);
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256) void pack_filter_kernel(const void* __restrict
     const int kk = q * E + e;
     u.e[e] = (ch < K && kk < Kg) ? w[static_cast<int64_t>(kk) * K + ch] : T(0);
   }
-  *reinterpret_cast<i32x4*>(wp + static_cast<int64_t>(p) * KgP + q * E) = u.v;
+  *reinterpret_cast<i32x4*>(wp + static_cast<int64_t>(p) * (KgP + E) + q * E) = u.v;
 }
 
 // ---------------------------------------------------------------- epilogues
@@ -153,24 +160,30 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Side-input chunk of output pixel m, channels ch0 .. ch0+15 (zero past K).
+__device__ inline i32x4 load_side_chunk(const ConvArgs& a, int m, int ch0, bool kvec) {
+  const int8_t* side = a.side + static_cast<int64_t>(m) * a.K + ch0;
+  if (kvec) return *reinterpret_cast<const i32x4*>(side);
+  union {
+    int8_t b[16];
+    i32x4 v;
+  } s;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s.b[e] = (ch0 + e < a.K) ? side[e] : int8_t(0);
+  return s.v;
+}
+
 // int8: TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel (cuDNN 8
-// order).  v[e] is the int32 accumulator of channel ch0 + e.
+// order).  v[e] is the int32 accumulator of channel ch0 + e; side_chunk holds
+// the int8 side input of the same 16 channels (ignored unless a.use_side).
 __device__ inline void epilogue_store_i8(const int32_t (&v)[16], const ConvArgs& a,
-                                         int m, int ch0, bool kvec) {
+                                         int m, int ch0, bool kvec, i32x4 side_chunk) {
   int8_t* y = static_cast<int8_t*>(a.y) + static_cast<int64_t>(m) * a.K + ch0;
-  const int8_t* side = a.use_side ? a.side + static_cast<int64_t>(m) * a.K + ch0 : nullptr;
   union {
     int8_t b[16];
     i32x4 v;
   } s, o;
-  if (side) {
-    if (kvec) {
-      s.v = *reinterpret_cast<const i32x4*>(side);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s.b[e] = (ch0 + e < a.K) ? side[e] : int8_t(0);
-    }
-  }
+  s.v = side_chunk;
   const float lo = a.relu ? 0.0f : -128.0f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -178,7 +191,7 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[16], const ConvArgs&
     const float b = (kvec || ch < a.K) ? a.bias[ch] : 0.0f;
     float t = static_cast<float>(v[e]);        // int32 -> fp32, nearest even
     t = t * a.cis;                             // (1) scale
-    if (side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);  // (2)
+    if (a.use_side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);  // (2)
     t = t + b;                                 // (3) bias
     t = __builtin_rintf(t);                    // round half to even
     t = __builtin_fminf(__builtin_fmaxf(t, lo), 127.0f);
@@ -317,10 +330,12 @@ __global__ __launch_bounds__(kThreads) void conv_general_kernel(ConvArgs a) {
   const T* __restrict__ xn =
       static_cast<const T*>(a.x) + static_cast<int64_t>(n) * a.H * a.W * a.C;
   // Packed filter row of this lane in MFMA tile 0; tile j adds 16 rows.
-  const T* __restrict__ wrow = static_cast<const T*>(a.wp) +
-                               static_cast<int64_t>(blockIdx.y * kTileN + col) * a.KgP +
+  const T* __restrict__ wrow = reinterpret_cast<const T*>(
+                                   static_cast<const char*>(a.wp) +
+                                   static_cast<int64_t>(blockIdx.y * kTileN + col) *
+                                       a.wrow_bytes) +
                                g * E;
-  const int64_t tile_stride = static_cast<int64_t>(16) * a.KgP;
+  const int64_t tile_stride = static_cast<int64_t>(16) * (a.wrow_bytes / sizeof(T));
 
   Acc acc[4];
 #pragma unroll
@@ -366,7 +381,8 @@ __global__ __launch_bounds__(kThreads) void conv_general_kernel(ConvArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[4 * j + i] = acc[j][i];
-    epilogue_store_i8(v, a, m, ch0, KVEC);
+    const i32x4 sc = a.use_side ? load_side_chunk(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
+    epilogue_store_i8(v, a, m, ch0, KVEC, sc);
   } else {
     float v[16];
 #pragma unroll
@@ -377,11 +393,431 @@ __global__ __launch_bounds__(kThreads) void conv_general_kernel(ConvArgs a) {
   }
 }
 
+// ------------------------------------------------ resident-filter conv
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer descriptor, gfx9 family
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offset past every extent: reads 0
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferDword3);
+}
+
+// Resident-filter kernel.  The workgroup's 64-channel slice of the packed
+// filter (64 padded rows, contiguous in global memory) is copied into LDS
+// with direct global->LDS 16-byte loads, so it crosses L2 once per workgroup
+// and costs no registers.  Each wave owns 16*PT consecutive output pixels x 64
+// channels: one LDS filter fragment feeds PT MFMAs and one patch fragment
+// feeds 4.  Patch fragments are raw buffer loads kept D k-steps ahead of the
+// MFMAs in a register ring; a tap that falls in the padding gets an offset
+// past the buffer's extent and reads zeros, so the gather has no branches.
+// The side input is loaded before the main loop and y is written with buffer
+// stores (pixels past M fall outside the extent and are dropped).
+// Requires C % (4 chunks) == 0 (a k-step never straddles a tap), K % 16 == 0
+// and x, y below 2 GiB.
+//
+// The packed rows' stride is an odd multiple of 16 bytes, so the 16 rows one
+// ds_read_b128 touches land in 16 different 16-byte bank groups.
+constexpr int kRfBN = 64;
+
+template <int DT, int PT, int D>
+__global__ __launch_bounds__(kThreads) void conv_rf_kernel(ConvArgs a) {
+  using T = typename Dt<DT>::T;
+  using Acc = typename Dt<DT>::Acc;
+  constexpr int E = Dt<DT>::kChunk;
+  constexpr int KSTEP = 4 * E;
+  constexpr int ES = static_cast<int>(sizeof(T));
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int RS = a.wrow_bytes;
+  const int ch0 = blockIdx.y * kRfBN + 16 * g;
+
+  // 1. Filter slice -> LDS: 64 * RS bytes = 4 * RS chunks of 16 bytes, i.e.
+  //    RS / 16 wave-wide 1 KiB copies, spread over the 4 waves.
+  {
+    const char* src = static_cast<const char*>(a.wp) +
+                      static_cast<int64_t>(blockIdx.y) * kRfBN * RS;
+    const int copies = RS / 16;
+    for (int i = wave; i < copies; i += 4)
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                       (lds_ptr_t)(smem + i * 1024), 16, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. Pixels of this lane (one per pixel tile) and their patch origins.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const int CB = a.C * ES;  // bytes per input pixel
+  const int mbase = blockIdx.x * (4 * 16 * PT) + wave * (16 * PT) + col;
+  int hb[PT], wb[PT], pbase[PT];
+#pragma unroll
+  for (int p = 0; p < PT; ++p) {
+    const int m = mbase + 16 * p;
+    const int mm = m < a.M ? m : 0;
+    const int wo = mm % a.Wo;
+    const int t = mm / a.Wo;
+    const int ho = t % a.Ho;
+    const int n = t / a.Ho;
+    // A pixel past M gets an origin no tap can bring back into the image.
+    hb[p] = m < a.M ? ho * a.sh - a.pt : -(1 << 20);
+    wb[p] = wo * a.sw - a.pl;
+    pbase[p] = n * a.H * a.W * CB + g * E * ES;
+  }
+
+  // 3. Side input of every pixel tile (zeros when unused: empty extent).
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, a.use_side ? a.side_bytes : 0u);
+  i32x4 side_frag[PT];
+#pragma unroll
+  for (int p = 0; p < PT; ++p)
+    side_frag[p] = __builtin_amdgcn_raw_buffer_load_b128(
+        sr, static_cast<uint32_t>((mbase + 16 * p) * a.K + ch0), 0, 0);
+
+  // 4. Patch-fragment ring: k-step ks -> tap (r, s), channel offset c0.
+  const int cs = a.C / KSTEP;
+  const int nks = a.R * a.S * cs;
+  auto issue = [&](int ks, i32x4(&f)[PT]) {
+    const int tap = ks / cs;
+    const int c0b = (ks - tap * cs) * KSTEP * ES;
+    const int r = tap / a.S;
+    const int s = tap - r * a.S;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int hi = hb[p] + r;
+      const int wi = wb[p] + s;
+      const bool ok = static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                      static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+      const uint32_t off = ok ? static_cast<uint32_t>(pbase[p] + (hi * a.W + wi) * CB + c0b)
+                              : kOutOfRange;
+      f[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+    }
+  };
+  i32x4 ring[D][PT];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nks) issue(d, ring[d]);
+
+  // The filter copy was issued before the PT side loads and the ring's loads;
+  // vector-memory loads retire in order, so once at most that many remain
+  // outstanding this wave's part of the copy has landed in LDS.
+  {
+    constexpr int after = PT * (D + 1);
+    static_assert(after < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((after & 15) | ((after >> 4) << 14) | (7 << 4) | (15 << 8));
+    __syncthreads();
+  }
+
+  Acc acc[PT][4];
+#pragma unroll
+  for (int p = 0; p < PT; ++p)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[p][j] = Acc{0, 0, 0, 0};
+
+  const char* arow = smem + col * RS + g * E * ES;
+  for (int ks0 = 0; ks0 < nks; ks0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int ks = ks0 + d;
+      if (ks < nks) {
+        i32x4 af[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          af[j] = *reinterpret_cast<const i32x4*>(arow + j * 16 * RS + ks * KSTEP * ES);
+#pragma unroll
+        for (int p = 0; p < PT; ++p)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[p][j] = mma_chunk(af[j], ring[d][p], acc[p][j], static_cast<Dt<DT>*>(nullptr));
+        if (ks + D < nks) issue(ks + D, ring[d]);
+      }
+    }
+  }
+
+  // 5. Fused epilogue and stores.
+  if (ch0 >= a.K) return;
+#pragma unroll
+  for (int p = 0; p < PT; ++p) {
+    const int m = mbase + 16 * p;
+    if constexpr (DT == FCONV_INT8) {
+      int32_t v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * j + i] = acc[p][j][i];
+      if (m < a.M) epilogue_store_i8(v, a, m, ch0, true, side_frag[p]);
+    } else {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * j + i] = acc[p][j][i];
+      if (m < a.M) epilogue_store_float<DT>(v, a, m, ch0, true);
+    }
+  }
+}
+
+// ------------------------------------------------------- streaming conv
+
+__device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint32_t shift) {
+  return (__umulhi(n, mul) + (add ? n : 0u)) >> shift;
+}
+
+// int8 epilogue of one 16-pixel tile for this lane's pixel and 16 channels
+// (cuDNN 8 order, TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel),
+// written with one buffer store; an out-of-range offset drops it.
+// Per output: cvt, mul, [side cvt, fma], add, rndne, med3 (clip), and a
+// v_cvt_pk_u8_f32 that converts the clipped integer + 128 and packs it into
+// its byte; one XOR per 4 bytes restores the signed encoding.
+template <bool SIDE>
+__device__ inline void stream_epilogue_i8(const i32x4 (&acc)[4], i32x4 side_chunk,
+                                          const float (&bias)[16], float cis, float sis,
+                                          float lo, __amdgpu_buffer_rsrc_t yr, uint32_t off) {
+  union {
+    int8_t b[16];
+    i32x4 v;
+  } sd;
+  sd.v = side_chunk;
+  uint32_t packed[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * j + i;
+      float v = static_cast<float>(acc[j][i]);  // int32 -> fp32, nearest even
+      v = v * cis;                              // (1) scale
+      if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, v);  // (2)
+      v = v + bias[e];                          // (3) bias
+      v = __builtin_rintf(v);                   // round half to even
+      v = __builtin_amdgcn_fmed3f(v, lo, 127.0f);  // clip (lo = 0 under ReLU)
+      word = __builtin_amdgcn_cvt_pk_u8_f32(v + 128.0f, i, word);  // exact: integer in [0,255]
+    }
+    packed[j] = word ^ 0x80808080u;
+  }
+  __builtin_amdgcn_raw_buffer_store_b128(
+      i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
+            static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])},
+      yr, off, 0, 0);
+}
+
+// Streaming kernel for int8 layers with a short reduction: R x S taps of CS
+// k-steps (64 channels each).  Persistent: one workgroup per CU.  Each wave
+// keeps its 64-channel slice of the packed filter in registers for the whole
+// kernel (no LDS traffic) and walks a contiguous range of 16-pixel tiles;
+// workgroup ranges are grouped by XCD so neighbouring tiles, which share
+// input rows, share an L2.  Per tile, the patch fragments of all k-steps are
+// buffer loads issued two tiles ahead; a tap outside the image gets an
+// offset past the extent and reads zeros.  Each iteration issues the current
+// tile's MFMAs and, in the same basic block, the previous tile's epilogue,
+// so the matrix cores and the VALU work overlap.  Offsets use 24-bit
+// multiplies (every operand and product here is far below 2^24 / 2^31).
+template <int R, int S, int CS, bool SIDE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void conv_stream_i8_kernel(ConvArgs a) {
+  constexpr int NKS = R * S * CS;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int ch0 = blockIdx.y * 64 + 16 * g;
+
+  const int G = gridDim.x;
+  const int bx = blockIdx.x;
+  const int b = (G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
+  const int t_begin = b * a.tiles / G;  // b * tiles < 2^31 (checked at plan time)
+  const int t_end = (b + 1) * a.tiles / G;
+  const int n_tiles = t_end - t_begin - wave > 0 ? (t_end - t_begin - wave + 3) / 4 : 0;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+
+  const int CB = a.C;          // bytes per input pixel
+  const int WCB = a.W * CB;    // bytes per input row
+  const int HWCB = a.H * WCB;  // bytes per image
+
+  // Tap offsets relative to the tile pixel's patch origin (uniform).
+  int delta[NKS];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int c = 0; c < CS; ++c) delta[(r * S + s) * CS + c] = r * WCB + s * CB + c * 64;
+
+  // Buffer offsets of tile k's patch fragments (past the extent when the tap
+  // falls outside the image or the tile outside this wave's range).
+  auto offsets = [&](int k, uint32_t(&o)[NKS]) {
+    const int t = t_begin + wave + 4 * k;
+    const uint32_t m = static_cast<uint32_t>(t * 16 + col);
+    const bool live = static_cast<unsigned>(k) < static_cast<unsigned>(n_tiles) &&
+                      m < static_cast<uint32_t>(a.M);
+    const uint32_t q = fast_div(m, a.wo_mul, a.wo_add, a.wo_shift);
+    const int wo = static_cast<int>(m) - __mul24(static_cast<int>(q), a.Wo);
+    const uint32_t n = fast_div(q, a.ho_mul, a.ho_add, a.ho_shift);
+    const int ho = static_cast<int>(q) - __mul24(static_cast<int>(n), a.Ho);
+    const int hb = __mul24(ho, a.sh) - a.pt;
+    const int wb = __mul24(wo, a.sw) - a.pl;
+    const int base = __mul24(static_cast<int>(n), HWCB) + __mul24(hb, WCB) +
+                     __mul24(wb, CB) + g * 16;
+    bool rok[R], cok[S];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      rok[r] = live && static_cast<unsigned>(hb + r) < static_cast<unsigned>(a.H);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      cok[s] = static_cast<unsigned>(wb + s) < static_cast<unsigned>(a.W);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int c = 0; c < CS; ++c) {
+          const int ks = (r * S + s) * CS + c;
+          o[ks] = (rok[r] && cok[s]) ? static_cast<uint32_t>(base + delta[ks]) : kOutOfRange;
+        }
+  };
+  auto issue = [&](int k, i32x4(&f)[NKS]) {
+    uint32_t o[NKS];
+    offsets(k, o);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) f[ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, o[ks], 0, 0);
+  };
+  // Output (and side-input) offset of tile k for this lane, or out of range;
+  // the uniform range test is folded into one unsigned compare.
+  auto out_off = [&](int k) -> uint32_t {
+    const int m = (t_begin + wave + 4 * k) * 16 + col;
+    const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(n_tiles) &&
+                    m < a.M && ch0 < a.K;
+    return ok ? static_cast<uint32_t>(__mul24(m, a.K) + ch0) : kOutOfRange;
+  };
+  auto issue_side = [&](int k) -> i32x4 {
+    if constexpr (SIDE) return __builtin_amdgcn_raw_buffer_load_b128(sr, out_off(k), 0, 0);
+    return i32x4{0, 0, 0, 0};
+  };
+
+  // The 64-channel filter slice crosses L2 once per workgroup: a direct
+  // global->LDS copy of its 64 padded rows, then every wave reads its
+  // fragments for all k-steps and the 4 MFMA tiles into registers.  The 16
+  // bias values of this lane's channels come in with four buffer loads
+  // (channels past K read 0).  All of it is waited for before the tile
+  // pipeline starts.
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int RS = a.wrow_bytes;
+  {
+    const char* src = static_cast<const char*>(a.wp) + static_cast<int64_t>(blockIdx.y) * 64 * RS;
+    for (int i = wave; i < RS / 16; i += 4)
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
+                                       (lds_ptr_t)(smem + i * 1024), 16, 0, 0);
+  }
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, static_cast<uint32_t>(a.K) * 4u);
+  float bias[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, static_cast<uint32_t>((ch0 + 4 * q) * 4), 0, 0));
+    bias[4 * q] = v.x;
+    bias[4 * q + 1] = v.y;
+    bias[4 * q + 2] = v.z;
+    bias[4 * q + 3] = v.w;
+  }
+  const float cis = a.cis, sis = a.sis, lo = a.relu ? 0.0f : -128.0f;
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
+  __syncthreads();
+  i32x4 Wf[NKS][4];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      Wf[ks][j] = *reinterpret_cast<const i32x4*>(smem + (j * 16 + col) * RS + ks * 64 + g * 16);
+
+  // Prologue: the same sequence of vector-memory operations one loop trip
+  // leaves behind -- tile loads, a (dropped) store, a side load -- so the
+  // wait counts the compiler derives for the loop hold from the first trip.
+  const i32x4 zero4 = i32x4{0, 0, 0, 0};
+  i32x4 bA[NKS], bB[NKS];
+  issue(0, bA);
+  __builtin_amdgcn_raw_buffer_store_b128(zero4, yr, kOutOfRange, 0, 0);
+  i32x4 sB = issue_side(-1);
+  issue(1, bB);
+  __builtin_amdgcn_raw_buffer_store_b128(zero4, yr, kOutOfRange, 0, 0);
+  i32x4 sA = issue_side(0);
+
+  i32x4 accA[4], accB[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) accB[j] = zero4;
+
+  // One half of a loop trip, software-pipelined by hand: the MFMAs of the
+  // tile in bX (into accX) are split by k-step into NKS chunks; each chunk
+  // also issues that k-step's refill load for tile k_load and finishes EPC of
+  // the 16 epilogue outputs of the previous tile (accY, side sY).  A
+  // scheduling barrier closes each chunk, so the VALU epilogue runs under the
+  // matrix-core work instead of before or after it.
+  constexpr int EPC = (16 + NKS - 1) / NKS;
+  auto half = [&](i32x4(&bX)[NKS], i32x4(&accX)[4], const i32x4(&accY)[4], i32x4 sY,
+                  int k_load, uint32_t off_prev) {
+    uint32_t o[NKS];
+    offsets(k_load, o);
+    union {
+      int8_t b[16];
+      i32x4 v;
+    } sd;
+    sd.v = sY;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        accX[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Wf[ks][j], bX[ks],
+                                                        ks == 0 ? zero4 : accX[j], 0, 0, 0);
+      bX[ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, o[ks], 0, 0);
+#pragma unroll
+      for (int e = ks * EPC; e < (ks + 1) * EPC && e < 16; ++e) {
+        // cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel)
+        float v = static_cast<float>(accY[e / 4][e % 4]);  // int32 -> fp32, nearest even
+        v = v * cis;                                        // (1) scale
+        if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, v);  // (2)
+        v = v + bias[e];                                    // (3) bias
+        v = __builtin_rintf(v);                             // round half to even
+        v = __builtin_amdgcn_fmed3f(v, lo, 127.0f);         // clip (lo = 0 under ReLU)
+        words[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(v + 128.0f, e % 4, words[e / 4]);
+      }
+      // Pin this chunk's outputs here: without it the arithmetic, which has
+      // no memory effects, is sunk to the store at the end of the half.
+      asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(
+        i32x4{static_cast<int32_t>(words[0] ^ 0x80808080u),
+              static_cast<int32_t>(words[1] ^ 0x80808080u),
+              static_cast<int32_t>(words[2] ^ 0x80808080u),
+              static_cast<int32_t>(words[3] ^ 0x80808080u)},
+        yr, off_prev, 0, 0);
+  };
+
+  // Two tiles per trip and no exit in between, so both halves see the same
+  // memory-operation history: half A computes tile k and finishes tile k-1,
+  // half B computes tile k+1 and finishes tile k.  A tile past the wave's
+  // range loads zeros and its store is dropped.
+  int k = 0;
+  for (; k < n_tiles; k += 2) {
+    half(bA, accA, accB, sB, k + 2, out_off(k - 1));
+    sB = issue_side(k + 1);
+    half(bB, accB, accA, sA, k + 3, out_off(k));
+    sA = issue_side(k + 2);
+  }
+  stream_epilogue_i8<SIDE>(accB, sB, bias, cis, sis, lo, yr, out_off(k - 1));
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <int DT>
 hipError_t launch_pack(const fconv_plan_s* p, const void* w, void* wp, hipStream_t s) {
-  const int64_t chunks = static_cast<int64_t>(p->Kp) * (p->KgP / p->chunk_elems);
+  const int64_t chunks = static_cast<int64_t>(p->Kp) * (p->KgP / p->chunk_elems + 1);
   const int blocks = static_cast<int>((chunks + 255) / 256);
   hipLaunchKernelGGL(pack_filter_kernel<DT>, dim3(blocks), dim3(256), 0, s, w, wp, p->d.K,
                      p->Kg, p->KgP, p->Kp);
@@ -408,6 +844,77 @@ hipError_t launch_general(const fconv_plan_s* p, const ConvArgs& a, hipStream_t 
   }
 }
 
+template <int DT, int PT, int D>
+hipError_t launch_rf_pt(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kRfBN) * a.wrow_bytes;
+  const auto kern = conv_rf_kernel<DT, PT, D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((p->M + 64 * PT - 1) / (64 * PT)),
+                  static_cast<unsigned>(p->Kp / kRfBN));
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_rf(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const int key = p->pixel_tiles * 100 + p->ring_depth;
+  switch (key) {
+    case 104: return launch_rf_pt<DT, 1, 4>(p, a, s);
+    case 109: return launch_rf_pt<DT, 1, 9>(p, a, s);
+    case 204: return launch_rf_pt<DT, 2, 4>(p, a, s);
+    case 209: return launch_rf_pt<DT, 2, 9>(p, a, s);
+    case 402: return launch_rf_pt<DT, 4, 2>(p, a, s);
+    case 404: return launch_rf_pt<DT, 4, 4>(p, a, s);
+    default: return launch_rf_pt<DT, 2, 4>(p, a, s);
+  }
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int R, int S, int CS>
+hipError_t launch_stream_shape(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const int cus = device_cu_count();
+  int grid = (a.tiles + 3) / 4;  // at least one tile per wave
+  if (grid > cus) grid = cus;
+  const dim3 g(static_cast<unsigned>(grid), static_cast<unsigned>(p->Kp / 64));
+  const size_t lds = static_cast<size_t>(64) * a.wrow_bytes;
+  if (a.use_side)
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true>), g, dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false>), g, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const int cs = p->d.C / 64;
+  if (p->d.R == 3 && p->d.S == 3 && cs == 1) return launch_stream_shape<3, 3, 1>(p, a, s);
+  if (p->d.R == 1 && p->d.S == 1) {
+    switch (cs) {
+      case 1: return launch_stream_shape<1, 1, 1>(p, a, s);
+      case 2: return launch_stream_shape<1, 1, 2>(p, a, s);
+      case 4: return launch_stream_shape<1, 1, 4>(p, a, s);
+      case 8: return launch_stream_shape<1, 1, 8>(p, a, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_pack_any(const fconv_plan_s* p, const void* w, void* wp, hipStream_t s) {
   switch (p->d.dtype) {
     case FCONV_INT8: return launch_pack<FCONV_INT8>(p, w, wp, s);
@@ -417,6 +924,14 @@ hipError_t launch_pack_any(const fconv_plan_s* p, const void* w, void* wp, hipSt
 }
 
 hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  if (p->variant == kStream) return launch_stream(p, a, s);
+  if (p->variant == kResidentFilter) {
+    switch (p->d.dtype) {
+      case FCONV_INT8: return launch_rf<FCONV_INT8>(p, a, s);
+      case FCONV_BF16: return launch_rf<FCONV_BF16>(p, a, s);
+      default: return launch_rf<FCONV_FP32>(p, a, s);
+    }
+  }
   switch (p->d.dtype) {
     case FCONV_INT8: return launch_general<FCONV_INT8>(p, a, s);
     case FCONV_BF16: return launch_general<FCONV_BF16>(p, a, s);
@@ -465,6 +980,14 @@ fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) 
   a.M = static_cast<int32_t>(p->M);
   a.Kg = p->Kg;
   a.KgP = p->KgP;
+  a.wrow_bytes = p->wrow_bytes;
+  a.x_bytes = static_cast<uint32_t>(p->x_elems * p->esize);
+  a.y_bytes = static_cast<uint32_t>(p->y_elems * p->esize);
+  a.side_bytes = static_cast<uint32_t>(p->y_elems);
+  a.wp_bytes = static_cast<uint32_t>(p->ws_bytes);
+  a.tiles = static_cast<int32_t>((p->M + 15) / 16);
+  a.wo_mul = p->wo_div.mul; a.wo_add = p->wo_div.add; a.wo_shift = p->wo_div.shift;
+  a.ho_mul = p->ho_div.mul; a.ho_add = p->ho_div.add; a.ho_shift = p->ho_div.shift;
   // TensorFlow's output kernel skips the side input when its scale is zero.
   a.use_side = p->op_side && args->side_input_scale != 0.0f;
   a.use_bias = p->op_bias;

@@ -73,17 +73,62 @@ fconv_status parse_ops(fconv_plan_s* p) {
   return FCONV_OK;
 }
 
-const char* general_kernel_name(int32_t dtype) {
-  switch (dtype) {
-    case FCONV_INT8: return "conv_general_i8";
-    case FCONV_BF16: return "conv_general_bf16";
-    default: return "conv_general_f32";
-  }
+const char* kernel_name(int32_t variant, int32_t dtype) {
+  static const char* names[3][3] = {
+      {"conv_general_i8", "conv_general_bf16", "conv_general_f32"},
+      {"conv_rf_i8", "conv_rf_bf16", "conv_rf_f32"},
+      {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"}};
+  return names[variant][dtype];
 }
 
+// LDS budget of the resident-filter kernel's 64-row filter slice: at most
+// this much, so that two workgroups still fit in a CU's 160 KiB.
+constexpr int64_t kRfMaxLds = 80 * 1024;
+
+// Kernel choice.  FCONV_FORCE_VARIANT=general (environment) pins the general
+// kernel, for A/B comparisons; FCONV_RF_PT=1|2|4 overrides the pixel tiles.
 void choose_variant(fconv_plan_s* p) {
+  const fconv_desc& d = p->d;
   p->variant = kGeneral;
-  p->kernel_name = general_kernel_name(p->d.dtype);
+  p->pixel_tiles = 1;
+  p->ring_depth = 0;
+  const int64_t rf_lds = 64 * static_cast<int64_t>(p->wrow_bytes);
+  const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
+  const char* force = getenv("FCONV_FORCE_VARIANT");
+  const bool force_general = force && strcmp(force, "general") == 0;
+  if (!force_general && p->load_mode == kLoadTap && d.K % 16 == 0 && rf_lds <= kRfMaxLds &&
+      x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31)) {
+    p->variant = kResidentFilter;
+    const int64_t nks = static_cast<int64_t>(p->Kg) / (4 * p->chunk_elems);
+    // Pixel tiles per wave vs ring depth: keep every k-step in flight when the
+    // reduction is short (3x3 over 64 channels: 9 k-steps), otherwise a
+    // 4-deep ring with more pixel reuse of each filter fragment.
+    if (nks <= 4) {
+      p->pixel_tiles = 2;
+      p->ring_depth = 4;
+    } else if (nks <= 9) {
+      p->pixel_tiles = 2;
+      p->ring_depth = 9;
+    } else {
+      p->pixel_tiles = 4;
+      p->ring_depth = 4;
+    }
+    const char* pt = getenv("FCONV_RF_PT");
+    const char* rd = getenv("FCONV_RF_DEPTH");
+    if (pt) p->pixel_tiles = atoi(pt);
+    if (rd) p->ring_depth = atoi(rd);
+    // int8 with a short reduction, in the shapes the streaming kernel is
+    // instantiated for (3x3 over 64 channels; 1x1 over 64..512): filter slice
+    // in registers.  Its tile split computes block * tiles in 32 bits.
+    const bool rf_only = force && strcmp(force, "rf") == 0;
+    const int32_t cs = d.C / 64;
+    const bool shape_ok = (d.R == 3 && d.S == 3 && cs == 1) ||
+                          (d.R == 1 && d.S == 1 && (cs == 1 || cs == 2 || cs == 4 || cs == 8));
+    const int64_t tiles = (p->M + 15) / 16;
+    if (!rf_only && d.dtype == FCONV_INT8 && shape_ok && tiles * 1024 < (int64_t{1} << 31))
+      p->variant = kStream;
+  }
+  p->kernel_name = kernel_name(p->variant, d.dtype);
 }
 
 bool aligned(const void* ptr, uintptr_t a) {
@@ -99,6 +144,16 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace
 
 namespace fconv {
+
+// s = ceil(log2 d), m = floor(2^(32+s) / d) + 1 (< 2^33).  For n < 2^31,
+// n*m / 2^(32+s) exceeds n/d by less than 2^-(s+1) <= 1/(2d), which never
+// reaches the next integer, so the floor is exact.
+FastDiv make_fast_div(uint32_t d) {
+  uint32_t s = 0;
+  while ((uint64_t{1} << s) < d) ++s;
+  const uint64_t m = ((uint64_t{1} << (32 + s)) / d) + 1;
+  return FastDiv{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), s};
+}
 
 fconv_status check_pack_args(const fconv_plan_s* p, const void* w,
                              const void* workspace, size_t workspace_bytes) {
@@ -195,13 +250,16 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
   p->Kg = static_cast<int32_t>(kg);
   p->KgP = static_cast<int32_t>(kgp);
   p->Kp = static_cast<int32_t>(kp);
-  p->ws_bytes = static_cast<size_t>(kp * kgp * p->esize);
+  p->wrow_bytes = static_cast<int32_t>(kgp * p->esize + 16);
+  p->ws_bytes = static_cast<size_t>(kp * p->wrow_bytes);
   if (d.C % kstep == 0)
     p->load_mode = kLoadTap;
   else if (d.C % p->chunk_elems == 0)
     p->load_mode = kLoadChunk;
   else
     p->load_mode = kLoadElem;
+  p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
+  p->ho_div = make_fast_div(static_cast<uint32_t>(p->Ho));
   choose_variant(p);
   *out = p;
   return FCONV_OK;

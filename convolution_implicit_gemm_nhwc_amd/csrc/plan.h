@@ -12,8 +12,17 @@ namespace fconv {
 // Kernel families.  Every plan can fall back to kGeneral; the others are
 // shape-specialised tilings chosen by choose_variant() in plan.cpp.
 enum Variant : int32_t {
-  kGeneral = 0,  // any shape: direct-from-global implicit GEMM, 64x64 tile
+  kGeneral = 0,        // any shape: direct-from-global implicit GEMM, 64x64 tile
+  kResidentFilter = 1, // 64-channel filter slice staged in LDS once per workgroup
+  kStream = 2,         // int8, short reduction: filter in registers, persistent
 };
+
+// Division by a runtime constant d for numerators below 2^31:
+// n / d = (umulhi(n, mul) + (add ? n : 0)) >> shift.
+struct FastDiv {
+  uint32_t mul, add, shift;
+};
+FastDiv make_fast_div(uint32_t d);
 
 // How the implicit-GEMM A operand (im2col row) is gathered, per 16-byte
 // chunk of the reduction dimension (r, s, c):
@@ -38,7 +47,11 @@ struct fconv_plan_s {
   int32_t Kp;     // K rounded up to a multiple of 64 (packed filter rows)
   int32_t load_mode;
   int32_t variant;
-  size_t ws_bytes;  // packed filter: Kp * KgP * esize
+  int32_t pixel_tiles;  // kResidentFilter: 16-pixel MFMA tiles per wave (1, 2, 4)
+  int32_t ring_depth;   // kResidentFilter: k-steps of patch loads in flight
+  int32_t wrow_bytes;   // packed filter row stride: KgP * esize + 16 (zero pad)
+  fconv::FastDiv wo_div, ho_div;
+  size_t ws_bytes;      // packed filter: Kp * wrow_bytes
   int64_t x_elems, y_elems, w_elems;
   const char* kernel_name;
 };

@@ -248,3 +248,58 @@ def test_pack_filter_then_prepacked_run_matches():
         a, _ = run_gpu(plan, dtype, x, w, bias, None, 2.0 ** -8, prepacked_ws=ws)
         b, _ = run_gpu(plan, dtype, x, w, bias, None, 2.0 ** -8)
         assert np.array_equal(a, b), dtype
+
+
+@pytest.mark.parametrize("variant", ["general", "rf"])
+@pytest.mark.parametrize("name", ["resnet_3x3_int8", "resnet_1x1_int8"])
+def test_workload_forced_variant(name, variant, monkeypatch):
+    """Every kernel family stays bit-exact on the layers another family is
+    normally chosen for (FCONV_FORCE_VARIANT is read at plan creation)."""
+    monkeypatch.setenv("FCONV_FORCE_VARIANT", variant)
+    L = wl.LAYERS[name]
+    inp, plan = _layer_case(L, N=4)
+    assert plan.kernel_name.startswith("conv_" + variant), plan.kernel_name
+    say("forced %s on %s" % (plan.kernel_name, name))
+    y, guards = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, inp.side, L.conv_input_scale,
+                        L.side_input_scale, guard=128)
+    assert guards
+    r = oracle_out(L.dtype, inp.x, inp.w, L.stride, L.padding, inp.bias, inp.side,
+                   L.conv_input_scale, L.side_input_scale, L.relu)
+    assert np.array_equal(y, r)
+
+
+@pytest.mark.parametrize("name", ["resnet_3x3_int8", "resnet_1x1_int8", "resnet_3x3s2_int8"])
+def test_graph_replay_matches_eager(name):
+    """A captured HIP graph of prepacked runs, replayed several times with
+    eager work and synchronisation in between, reproduces the eager output
+    on every replay."""
+    dev = device()
+    L = wl.LAYERS[name]
+    inp, plan = _layer_case(L, N=4)
+    x, w = to_dev(inp.x, dev), to_dev(inp.w, dev)
+    bias, side = to_dev(inp.bias, dev), to_dev(inp.side, dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    plan.pack_filter(w, ws)
+    y_eager = torch.empty(plan.out_shape, dtype=torch.int8, device=dev)
+    plan.run(x, w, y_eager, ws, bias=bias, side=side, conv_input_scale=L.conv_input_scale,
+             side_input_scale=L.side_input_scale, prepacked=True)
+    torch.cuda.synchronize()
+    ref = y_eager.cpu()
+    y = torch.zeros(plan.out_shape, dtype=torch.int8, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    args = plan.make_args(x, w, y, ws, bias=bias, side=side,
+                          conv_input_scale=L.conv_input_scale,
+                          side_input_scale=L.side_input_scale, prepacked=True)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(3):
+                assert plan.run_args(args, s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), ref), "replay %d differs" % rep
