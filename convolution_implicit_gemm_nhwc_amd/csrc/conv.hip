@@ -560,22 +560,200 @@ __global__ __launch_bounds__(kThreads) void conv_rf_kernel(ConvArgs a) {
   }
 }
 
-// ------------------------------------------------------- streaming conv
+// ----------------------------------------------------------- tiled conv
 
+// n / d for n < 2^31 with host-computed (mul, add, shift); see make_fast_div.
 __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint32_t shift) {
   return (__umulhi(n, mul) + (add ? n : 0u)) >> shift;
 }
 
-// int8 epilogue of one 16-pixel tile for this lane's pixel and 16 channels
-// (cuDNN 8 order, TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel),
+// LDS-tiled implicit GEMM for reductions too long to keep the filter slice
+// resident (bf16 / fp32 256-channel layers, int8 strided layers).  Workgroup
+// tile: 128 pixels x 128 output channels, 4 waves in a 2 x 2 grid of 64 x 64.
+// The reduction advances in stages of 128 bytes (one filter tap, 128 bytes of
+// its channels; two MFMA k-steps).  Per stage every thread fetches 4 pixel-row
+// and 4 filter-row pieces of 16 bytes with buffer loads -- taps in the
+// padding and rows past M or Kp read zeros -- two stages ahead into a
+// register ring, and writes a fetched stage into one half of a double-buffered
+// LDS area.  LDS rows are 144 bytes (128 + 16 pad, an odd multiple of 16):
+// the 16 rows one ds_read_b128 touches fall in distinct bank groups.  Each
+// wave does a 4 x 4 grid of 16x16 MFMAs per k-step: 8 fragment reads feed 16
+// MFMAs.
+constexpr int kTileBM = 128, kTileBN = 128, kTileStage = 128, kTileRow = kTileStage + 16;
+
+template <int DT, bool KVEC>
+__global__ __launch_bounds__(kThreads) void conv_tile_kernel(ConvArgs a) {
+  using Acc = typename Dt<DT>::Acc;
+  constexpr int E = Dt<DT>::kChunk;
+  constexpr int ES = 16 / E;
+  constexpr int SE = kTileStage / ES;  // reduction elements per stage
+  __shared__ __attribute__((aligned(16))) char lds[2][(kTileBM + kTileBN) * kTileRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = lane >> 4, col = lane & 15;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+
+  // Loader role: rows r0 + 32h (h = 0..3) of both tiles, 16-byte piece q.
+  const int q = tid & 7;
+  const int r0 = tid >> 3;
+  int hb[4], wb[4], pbase[4];
+  uint32_t wbase[4];
+  const int RS = a.wrow_bytes;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int m = blockIdx.x * kTileBM + r0 + 32 * h;
+    const int mm = m < a.M ? m : 0;
+    const uint32_t qq = fast_div(static_cast<uint32_t>(mm), a.wo_mul, a.wo_add, a.wo_shift);
+    const int wo = mm - static_cast<int>(qq) * a.Wo;
+    const uint32_t n = fast_div(qq, a.ho_mul, a.ho_add, a.ho_shift);
+    const int ho = static_cast<int>(qq) - static_cast<int>(n) * a.Ho;
+    hb[h] = m < a.M ? ho * a.sh - a.pt : -(1 << 20);
+    wb[h] = wo * a.sw - a.pl;
+    pbase[h] = static_cast<int>(n) * a.H * a.W * a.C * ES + q * 16;
+    wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + r0 + 32 * h) * RS + q * 16);
+  }
+
+  const int cs = a.C / SE;  // stages per filter tap
+  const int nst = a.R * a.S * cs;
+  auto fetch = [&](int st, i32x4(&px)[4], i32x4(&fl)[4]) {
+    const int tap = st / cs;
+    const int c0b = (st - tap * cs) * kTileStage;
+    const int r = tap / a.S;
+    const int s = tap - r * a.S;
+    const bool live = st < nst;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int hi = hb[h] + r, wi = wb[h] + s;
+      const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                      static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+      const uint32_t off =
+          ok ? static_cast<uint32_t>(pbase[h] + (hi * a.W + wi) * a.C * ES + c0b) : kOutOfRange;
+      px[h] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+      fl[h] = __builtin_amdgcn_raw_buffer_load_b128(
+          wr, live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0);
+    }
+  };
+  auto stash = [&](int buf, const i32x4(&px)[4], const i32x4(&fl)[4]) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      *reinterpret_cast<i32x4*>(&lds[buf][(r0 + 32 * h) * kTileRow + q * 16]) = px[h];
+      *reinterpret_cast<i32x4*>(&lds[buf][(kTileBM + r0 + 32 * h) * kTileRow + q * 16]) = fl[h];
+    }
+  };
+
+  Acc acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* pl = &lds[buf][(wm * 64 + col) * kTileRow + kk * 64 + g * 16];
+      const char* fb = &lds[buf][(kTileBM + wn * 64 + col) * kTileRow + kk * 64 + g * 16];
+      i32x4 pf[4], ff[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileRow);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ff[j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileRow);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mma_chunk(ff[j], pf[i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
+    }
+  };
+
+  // Two stages of loads in flight (registers A and B alternate), one stage
+  // being computed from LDS.
+  // Stages go in pairs with no exit in between (one back-edge keeps the
+  // accumulators in place); fetches past the last stage read zeros.
+  i32x4 pxA[4], flA[4], pxB[4], flB[4];
+  fetch(0, pxA, flA);
+  fetch(1, pxB, flB);
+  stash(0, pxA, flA);
+  __syncthreads();
+  for (int st = 0; st + 2 <= nst; st += 2) {
+    fetch(st + 2, pxA, flA);
+    compute(0);          // stage st
+    stash(1, pxB, flB);  // stage st+1
+    __syncthreads();
+    fetch(st + 3, pxB, flB);
+    compute(1);          // stage st+1
+    stash(0, pxA, flA);  // stage st+2
+    __syncthreads();
+  }
+  if (nst & 1) compute(0);  // the last stage, already in buffer 0
+
+  const int ch0 = blockIdx.y * kTileBN + wn * 64 + 16 * g;
+  if (ch0 >= a.K) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+    if (m >= a.M) continue;
+    if constexpr (DT == FCONV_INT8) {
+      int32_t v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      const i32x4 sc = a.use_side ? load_side_chunk(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
+      epilogue_store_i8(v, a, m, ch0, KVEC, sc);
+    } else {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      epilogue_store_float<DT>(v, a, m, ch0, KVEC);
+    }
+  }
+}
+
+// ------------------------------------------------------- streaming conv
+
+// Requantisation of one output, cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc,
+// BiasActivationOutputKernel): (float)acc * cis, + side * sis as one fused
+// multiply-add, + bias, each an fp32 operation.  Round half to even and clip
+// are done together: adding 1.5 * 2^23 rounds t to the nearest integer (ties
+// to even) into the low mantissa bits, exactly for |t| < 2^22, and monotonically
+// beyond, where the clip saturates anyway; a med3 against the two biased
+// bounds clips, and the low byte of the result's bit pattern is then the int8
+// value (two's complement).  Checked exhaustively over every finite fp32 t.
+// `lo_b` / `hi_b` are 1.5*2^23 + (ReLU ? 0 : -128) and 1.5*2^23 + 127.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+template <bool SIDE>
+__device__ inline uint32_t requant_i8_bits(int32_t acc, int8_t side, float bias, float cis,
+                                           float sis, float lo_b, float hi_b) {
+  float v = static_cast<float>(acc);  // int32 -> fp32, nearest even
+  v = v * cis;                        // (1) scale
+  if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(side), sis, v);  // (2) side
+  v = v + bias;                       // (3) bias
+  v = v + kRoundMagic;                // round half to even
+  v = __builtin_amdgcn_fmed3f(v, lo_b, hi_b);  // clip
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Low bytes of two / of two pairs packed with v_perm_b32.
+__device__ inline uint32_t pack_pair(uint32_t lo_val, uint32_t hi_val) {
+  return __builtin_amdgcn_perm(hi_val, lo_val, 0x0c0c0400u);  // [lo.b0, hi.b0, 0, 0]
+}
+__device__ inline uint32_t pack_word(uint32_t lo_pair, uint32_t hi_pair) {
+  return __builtin_amdgcn_perm(hi_pair, lo_pair, 0x05040100u);  // [lo.b0, lo.b1, hi.b0, hi.b1]
+}
+
+// int8 epilogue of one 16-pixel tile for this lane's pixel and 16 channels,
 // written with one buffer store; an out-of-range offset drops it.
-// Per output: cvt, mul, [side cvt, fma], add, rndne, med3 (clip), and a
-// v_cvt_pk_u8_f32 that converts the clipped integer + 128 and packs it into
-// its byte; one XOR per 4 bytes restores the signed encoding.
 template <bool SIDE>
 __device__ inline void stream_epilogue_i8(const i32x4 (&acc)[4], i32x4 side_chunk,
                                           const float (&bias)[16], float cis, float sis,
-                                          float lo, __amdgpu_buffer_rsrc_t yr, uint32_t off) {
+                                          float lo_b, float hi_b, __amdgpu_buffer_rsrc_t yr,
+                                          uint32_t off) {
   union {
     int8_t b[16];
     i32x4 v;
@@ -584,19 +762,12 @@ __device__ inline void stream_epilogue_i8(const i32x4 (&acc)[4], i32x4 side_chun
   uint32_t packed[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t word = 0;
+    uint32_t vb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * j + i;
-      float v = static_cast<float>(acc[j][i]);  // int32 -> fp32, nearest even
-      v = v * cis;                              // (1) scale
-      if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, v);  // (2)
-      v = v + bias[e];                          // (3) bias
-      v = __builtin_rintf(v);                   // round half to even
-      v = __builtin_amdgcn_fmed3f(v, lo, 127.0f);  // clip (lo = 0 under ReLU)
-      word = __builtin_amdgcn_cvt_pk_u8_f32(v + 128.0f, i, word);  // exact: integer in [0,255]
-    }
-    packed[j] = word ^ 0x80808080u;
+    for (int i = 0; i < 4; ++i)
+      vb[i] = requant_i8_bits<SIDE>(acc[j][i], sd.b[4 * j + i], bias[4 * j + i], cis, sis,
+                                    lo_b, hi_b);
+    packed[j] = pack_word(pack_pair(vb[0], vb[1]), pack_pair(vb[2], vb[3]));
   }
   __builtin_amdgcn_raw_buffer_store_b128(
       i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
@@ -700,12 +871,20 @@ void conv_stream_i8_kernel(ConvArgs a) {
     return i32x4{0, 0, 0, 0};
   };
 
+  // The first two tiles' patch fragments and side inputs are issued first,
+  // so their latency overlaps the filter staging below.
+  const i32x4 zero4 = i32x4{0, 0, 0, 0};
+  i32x4 bA[NKS], bB[NKS];
+  issue(0, bA);
+  issue(1, bB);
+  i32x4 sB = issue_side(-1);  // tile -1: out of range, reads zeros
+  i32x4 sA = issue_side(0);
+
   // The 64-channel filter slice crosses L2 once per workgroup: a direct
   // global->LDS copy of its 64 padded rows, then every wave reads its
   // fragments for all k-steps and the 4 MFMA tiles into registers.  The 16
   // bias values of this lane's channels come in with four buffer loads
-  // (channels past K read 0).  All of it is waited for before the tile
-  // pipeline starts.
+  // (channels past K read 0).
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int RS = a.wrow_bytes;
   {
@@ -725,7 +904,8 @@ void conv_stream_i8_kernel(ConvArgs a) {
     bias[4 * q + 2] = v.z;
     bias[4 * q + 3] = v.w;
   }
-  const float cis = a.cis, sis = a.sis, lo = a.relu ? 0.0f : -128.0f;
+  const float cis = a.cis, sis = a.sis;
+  const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
   __syncthreads();
   i32x4 Wf[NKS][4];
@@ -734,18 +914,6 @@ void conv_stream_i8_kernel(ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       Wf[ks][j] = *reinterpret_cast<const i32x4*>(smem + (j * 16 + col) * RS + ks * 64 + g * 16);
-
-  // Prologue: the same sequence of vector-memory operations one loop trip
-  // leaves behind -- tile loads, a (dropped) store, a side load -- so the
-  // wait counts the compiler derives for the loop hold from the first trip.
-  const i32x4 zero4 = i32x4{0, 0, 0, 0};
-  i32x4 bA[NKS], bB[NKS];
-  issue(0, bA);
-  __builtin_amdgcn_raw_buffer_store_b128(zero4, yr, kOutOfRange, 0, 0);
-  i32x4 sB = issue_side(-1);
-  issue(1, bB);
-  __builtin_amdgcn_raw_buffer_store_b128(zero4, yr, kOutOfRange, 0, 0);
-  i32x4 sA = issue_side(0);
 
   i32x4 accA[4], accB[4];
 #pragma unroll
@@ -767,6 +935,7 @@ void conv_stream_i8_kernel(ConvArgs a) {
       i32x4 v;
     } sd;
     sd.v = sY;
+    uint32_t pairs[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     uint32_t words[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -775,27 +944,25 @@ void conv_stream_i8_kernel(ConvArgs a) {
         accX[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Wf[ks][j], bX[ks],
                                                         ks == 0 ? zero4 : accX[j], 0, 0, 0);
       bX[ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, o[ks], 0, 0);
+      // EPC is even, so a chunk finishes whole pairs of outputs.
 #pragma unroll
-      for (int e = ks * EPC; e < (ks + 1) * EPC && e < 16; ++e) {
-        // cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel)
-        float v = static_cast<float>(accY[e / 4][e % 4]);  // int32 -> fp32, nearest even
-        v = v * cis;                                        // (1) scale
-        if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, v);  // (2)
-        v = v + bias[e];                                    // (3) bias
-        v = __builtin_rintf(v);                             // round half to even
-        v = __builtin_amdgcn_fmed3f(v, lo, 127.0f);         // clip (lo = 0 under ReLU)
-        words[e / 4] = __builtin_amdgcn_cvt_pk_u8_f32(v + 128.0f, e % 4, words[e / 4]);
+      for (int e = ks * EPC; e < (ks + 1) * EPC && e < 16; e += 2) {
+        const uint32_t v0 = requant_i8_bits<SIDE>(accY[e / 4][e % 4], sd.b[e], bias[e], cis,
+                                                  sis, lo_b, hi_b);
+        const uint32_t v1 = requant_i8_bits<SIDE>(accY[e / 4][e % 4 + 1], sd.b[e + 1],
+                                                  bias[e + 1], cis, sis, lo_b, hi_b);
+        pairs[e / 2] = pack_pair(v0, v1);
+        if (e % 4 == 2) words[e / 4] = pack_word(pairs[e / 2 - 1], pairs[e / 2]);
       }
       // Pin this chunk's outputs here: without it the arithmetic, which has
       // no memory effects, is sunk to the store at the end of the half.
-      asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]));
+      asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]),
+                   "+v"(pairs[0]), "+v"(pairs[2]), "+v"(pairs[4]), "+v"(pairs[6]));
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_raw_buffer_store_b128(
-        i32x4{static_cast<int32_t>(words[0] ^ 0x80808080u),
-              static_cast<int32_t>(words[1] ^ 0x80808080u),
-              static_cast<int32_t>(words[2] ^ 0x80808080u),
-              static_cast<int32_t>(words[3] ^ 0x80808080u)},
+        i32x4{static_cast<int32_t>(words[0]), static_cast<int32_t>(words[1]),
+              static_cast<int32_t>(words[2]), static_cast<int32_t>(words[3])},
         yr, off_prev, 0, 0);
   };
 
@@ -810,7 +977,7 @@ void conv_stream_i8_kernel(ConvArgs a) {
     half(bB, accB, accA, sA, k + 3, out_off(k));
     sA = issue_side(k + 2);
   }
-  stream_epilogue_i8<SIDE>(accB, sB, bias, cis, sis, lo, yr, out_off(k - 1));
+  stream_epilogue_i8<SIDE>(accB, sB, bias, cis, sis, lo_b, hi_b, yr, out_off(k - 1));
 }
 
 // ------------------------------------------------------------- dispatch
@@ -923,8 +1090,23 @@ hipError_t launch_pack_any(const fconv_plan_s* p, const void* w, void* wp, hipSt
   }
 }
 
+template <int DT>
+hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((p->M + kTileBM - 1) / kTileBM),
+                  static_cast<unsigned>((p->Kp + kTileBN - 1) / kTileBN));
+  hipLaunchKernelGGL((conv_tile_kernel<DT, true>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
   if (p->variant == kStream) return launch_stream(p, a, s);
+  if (p->variant == kTiled) {
+    switch (p->d.dtype) {
+      case FCONV_INT8: return launch_tile<FCONV_INT8>(p, a, s);
+      case FCONV_BF16: return launch_tile<FCONV_BF16>(p, a, s);
+      default: return launch_tile<FCONV_FP32>(p, a, s);
+    }
+  }
   if (p->variant == kResidentFilter) {
     switch (p->d.dtype) {
       case FCONV_INT8: return launch_rf<FCONV_INT8>(p, a, s);

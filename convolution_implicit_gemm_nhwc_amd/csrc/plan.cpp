@@ -74,10 +74,11 @@ fconv_status parse_ops(fconv_plan_s* p) {
 }
 
 const char* kernel_name(int32_t variant, int32_t dtype) {
-  static const char* names[3][3] = {
+  static const char* names[4][3] = {
       {"conv_general_i8", "conv_general_bf16", "conv_general_f32"},
       {"conv_rf_i8", "conv_rf_bf16", "conv_rf_f32"},
-      {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"}};
+      {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"},
+      {"conv_tile_i8", "conv_tile_bf16", "conv_tile_f32"}};
   return names[variant][dtype];
 }
 
@@ -96,8 +97,19 @@ void choose_variant(fconv_plan_s* p) {
   const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
   const char* force = getenv("FCONV_FORCE_VARIANT");
   const bool force_general = force && strcmp(force, "general") == 0;
-  if (!force_general && p->load_mode == kLoadTap && d.K % 16 == 0 && rf_lds <= kRfMaxLds &&
-      x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31)) {
+  const bool force_tile = force && strcmp(force, "tile") == 0;
+  const bool sizes_ok = x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31) &&
+                        static_cast<int64_t>(p->ws_bytes) < (int64_t{1} << 31);
+  // Long tap-aligned reductions (more than 9 k-steps of 64 bytes) whose
+  // channels fill whole 128-byte stages: the LDS-tiled kernel.
+  const bool force_rf = force && strcmp(force, "rf") == 0;
+  const int64_t ksteps = p->Kg / (4 * p->chunk_elems);
+  const bool tile_ok = (static_cast<int64_t>(d.C) * p->esize) % 128 == 0;
+  if (!force_general && !force_rf && p->load_mode == kLoadTap && d.K % 16 == 0 && sizes_ok &&
+      tile_ok && (ksteps > 9 || rf_lds > kRfMaxLds || force_tile)) {
+    p->variant = kTiled;
+  } else if (!force_general && p->load_mode == kLoadTap && d.K % 16 == 0 && rf_lds <= kRfMaxLds &&
+      sizes_ok) {
     p->variant = kResidentFilter;
     const int64_t nks = static_cast<int64_t>(p->Kg) / (4 * p->chunk_elems);
     // Pixel tiles per wave vs ring depth: keep every k-step in flight when the

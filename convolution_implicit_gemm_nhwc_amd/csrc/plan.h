@@ -15,6 +15,7 @@ enum Variant : int32_t {
   kGeneral = 0,        // any shape: direct-from-global implicit GEMM, 64x64 tile
   kResidentFilter = 1, // 64-channel filter slice staged in LDS once per workgroup
   kStream = 2,         // int8, short reduction: filter in registers, persistent
+  kTiled = 3,          // 128x128 LDS-tiled implicit GEMM, long reductions
 };
 
 // Division by a runtime constant d for numerators below 2^31:

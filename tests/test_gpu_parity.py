@@ -250,11 +250,14 @@ def test_pack_filter_then_prepacked_run_matches():
         assert np.array_equal(a, b), dtype
 
 
-@pytest.mark.parametrize("variant", ["general", "rf"])
-@pytest.mark.parametrize("name", ["resnet_3x3_int8", "resnet_1x1_int8"])
+@pytest.mark.parametrize("name,variant", [
+    ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"),
+    ("resnet_1x1_int8", "general"), ("resnet_1x1_int8", "rf"), ("resnet_1x1_int8", "tile"),
+    ("resnet_3x3s2_int8", "general"), ("resnet_3x3s2_int8", "rf")])
 def test_workload_forced_variant(name, variant, monkeypatch):
     """Every kernel family stays bit-exact on the layers another family is
-    normally chosen for (FCONV_FORCE_VARIANT is read at plan creation)."""
+    normally chosen for (FCONV_FORCE_VARIANT is read at plan creation; the
+    tiled kernel needs channel rows of whole 128-byte stages)."""
     monkeypatch.setenv("FCONV_FORCE_VARIANT", variant)
     L = wl.LAYERS[name]
     inp, plan = _layer_case(L, N=4)
