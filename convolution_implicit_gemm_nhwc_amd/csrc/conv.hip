@@ -35,12 +35,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "plan.h"
 
 namespace fconv {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -116,6 +119,9 @@ struct ConvArgs {
   // m / Wo and q / Ho by multiply-high: q = (umulhi(n, mul) + (add ? n : 0)) >> shift
   uint32_t wo_mul, wo_add, wo_shift, ho_mul, ho_add, ho_shift;
   int32_t use_side, use_bias, use_bn, relu;
+  // Row-halo kernel: output rows per workgroup and rows of its first phase
+  // (set by its launcher).
+  int32_t halo_rows, halo_rows_a;
 };
 
 // ------------------------------------------------------------ filter repack
@@ -718,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void conv_tile_kernel(ConvArgs a) {
 
 // ------------------------------------------------------- streaming conv
 
-// Requantisation of one output, cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc,
+// int8 requantisation, cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc,
 // BiasActivationOutputKernel): (float)acc * cis, + side * sis as one fused
 // multiply-add, + bias, each an fp32 operation.  Round half to even and clip
 // are done together: adding 1.5 * 2^23 rounds t to the nearest integer (ties
@@ -728,17 +734,20 @@ __global__ __launch_bounds__(kThreads) void conv_tile_kernel(ConvArgs a) {
 // value (two's complement).  Checked exhaustively over every finite fp32 t.
 // `lo_b` / `hi_b` are 1.5*2^23 + (ReLU ? 0 : -128) and 1.5*2^23 + 127.
 constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
-template <bool SIDE>
-__device__ inline uint32_t requant_i8_bits(int32_t acc, int8_t side, float bias, float cis,
-                                           float sis, float lo_b, float hi_b) {
-  float v = static_cast<float>(acc);  // int32 -> fp32, nearest even
-  v = v * cis;                        // (1) scale
-  if constexpr (SIDE) v = __builtin_fmaf(static_cast<float>(side), sis, v);  // (2) side
-  v = v + bias;                       // (3) bias
-  v = v + kRoundMagic;                // round half to even
-  v = __builtin_amdgcn_fmed3f(v, lo_b, hi_b);  // clip
-  return __builtin_bit_cast(uint32_t, v);
+
+// Scheduling pattern of one k-step chunk: each of its MFMAs followed by up
+// to 4 VALU instructions, which issue while the matrix core works on the
+// MFMA (a single wave per SIMD issues in order), then the chunk's fragment
+// load.
+template <int NMFMA = 4>
+__device__ inline void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+  }
 }
+
 // Low bytes of two / of two pairs packed with v_perm_b32.
 __device__ inline uint32_t pack_pair(uint32_t lo_val, uint32_t hi_val) {
   return __builtin_amdgcn_perm(hi_val, lo_val, 0x0c0c0400u);  // [lo.b0, hi.b0, 0, 0]
@@ -747,61 +756,150 @@ __device__ inline uint32_t pack_word(uint32_t lo_pair, uint32_t hi_pair) {
   return __builtin_amdgcn_perm(hi_pair, lo_pair, 0x05040100u);  // [lo.b0, lo.b1, hi.b0, hi.b1]
 }
 
-// int8 epilogue of one 16-pixel tile for this lane's pixel and 16 channels,
+// One lane's NOUT/4 packed output words with a single buffer store.
+template <int NOUT>
+__device__ inline void store_words(const uint32_t (&w)[NOUT / 4], __amdgpu_buffer_rsrc_t yr,
+                                   uint32_t off) {
+  if constexpr (NOUT == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]),
+              static_cast<int32_t>(w[2]), static_cast<int32_t>(w[3])},
+        yr, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(
+        i32x2{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1])}, yr, off, 0, 0);
+}
+
+// Requantisation of a lane's NOUT (8 or 16) outputs, organised by stage so
+// that a streaming kernel can spread it over the k-steps of the next tile:
+// a stage runs one operation on 8 or 16 outputs at once, so the values are
+// independent chains and every operation's input was produced a whole k-step
+// earlier (VALU latency stays hidden).  Stages, in order:
+//   cvt   8 accumulators out of the accumulation registers -> fp32 (NOUT/8 stages)
+//   mul   * conv_input_scale
+//   side  8 outputs: side byte -> fp32, fused multiply-add by sis (NOUT/8
+//         stages; none without a side input)
+//   bias  + bias
+//   magic + 1.5 * 2^23 (round half to even)
+//   med3  clip
+//   pack  byte packing into NOUT/4 words
+template <bool SIDE, int NOUT>
+struct EpiI8 {
+  static constexpr int kCvt = NOUT / 8;
+  static constexpr int kSide = SIDE ? NOUT / 8 : 0;
+  static constexpr int kStages = kCvt + 1 + kSide + 4;
+  float t[NOUT];
+  uint32_t w[NOUT / 4];
+
+  __device__ inline void stage(int st, const i32x4 (&acc)[NOUT / 4], i32x4 side_chunk,
+                               const float (&bias)[NOUT], float cis, float sis, float lo_b,
+                               float hi_b) {
+    union {
+      int8_t b[16];
+      i32x4 v;
+    } sd;
+    sd.v = side_chunk;
+    if (st < kCvt) {
+#pragma unroll
+      for (int e = 8 * st; e < 8 * st + 8; ++e) t[e] = static_cast<float>(acc[e / 4][e % 4]);
+      return;
+    }
+    st -= kCvt;
+    if (st == 0) {
+#pragma unroll
+      for (int e = 0; e < NOUT; ++e) t[e] = t[e] * cis;
+      return;
+    }
+    st -= 1;
+    if (st < kSide) {
+#pragma unroll
+      for (int e = 8 * st; e < 8 * st + 8; ++e)
+        t[e] = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, t[e]);
+      return;
+    }
+    st -= kSide;
+    switch (st) {
+      case 0:
+#pragma unroll
+        for (int e = 0; e < NOUT; ++e) t[e] = t[e] + bias[e];
+        break;
+      case 1:
+#pragma unroll
+        for (int e = 0; e < NOUT; ++e) t[e] = t[e] + kRoundMagic;
+        break;
+      case 2:
+#pragma unroll
+        for (int e = 0; e < NOUT; ++e) t[e] = __builtin_amdgcn_fmed3f(t[e], lo_b, hi_b);
+        break;
+      default:
+#pragma unroll
+        for (int j = 0; j < NOUT / 4; ++j)
+          w[j] = pack_word(pack_pair(__builtin_bit_cast(uint32_t, t[4 * j]),
+                                     __builtin_bit_cast(uint32_t, t[4 * j + 1])),
+                           pack_pair(__builtin_bit_cast(uint32_t, t[4 * j + 2]),
+                                     __builtin_bit_cast(uint32_t, t[4 * j + 3])));
+        break;
+    }
+  }
+  // Keep the values produced so far in registers at this point of the
+  // instruction stream (the arithmetic has no memory effects and would
+  // otherwise be sunk to the store).
+  __device__ inline void pin() {
+#pragma unroll
+    for (int i = 0; i < NOUT; i += 8)
+      asm volatile("" : "+v"(t[i]), "+v"(t[i + 1]), "+v"(t[i + 2]), "+v"(t[i + 3]),
+                   "+v"(t[i + 4]), "+v"(t[i + 5]), "+v"(t[i + 6]), "+v"(t[i + 7]));
+#pragma unroll
+    for (int j = 0; j < NOUT / 4; ++j) asm volatile("" : "+v"(w[j]));
+  }
+};
+
+// Whole int8 epilogue of one tile for this lane's pixel and NOUT channels,
 // written with one buffer store; an out-of-range offset drops it.
-template <bool SIDE>
-__device__ inline void stream_epilogue_i8(const i32x4 (&acc)[4], i32x4 side_chunk,
-                                          const float (&bias)[16], float cis, float sis,
+template <bool SIDE, int NOUT>
+__device__ inline void stream_epilogue_i8(const i32x4 (&acc)[NOUT / 4], i32x4 side_chunk,
+                                          const float (&bias)[NOUT], float cis, float sis,
                                           float lo_b, float hi_b, __amdgpu_buffer_rsrc_t yr,
                                           uint32_t off) {
-  union {
-    int8_t b[16];
-    i32x4 v;
-  } sd;
-  sd.v = side_chunk;
-  uint32_t packed[4];
+  EpiI8<SIDE, NOUT> ep;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t vb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vb[i] = requant_i8_bits<SIDE>(acc[j][i], sd.b[4 * j + i], bias[4 * j + i], cis, sis,
-                                    lo_b, hi_b);
-    packed[j] = pack_word(pack_pair(vb[0], vb[1]), pack_pair(vb[2], vb[3]));
-  }
-  __builtin_amdgcn_raw_buffer_store_b128(
-      i32x4{static_cast<int32_t>(packed[0]), static_cast<int32_t>(packed[1]),
-            static_cast<int32_t>(packed[2]), static_cast<int32_t>(packed[3])},
-      yr, off, 0, 0);
+  for (int st = 0; st < EpiI8<SIDE, NOUT>::kStages; ++st)
+    ep.stage(st, acc, side_chunk, bias, cis, sis, lo_b, hi_b);
+  store_words<NOUT>(ep.w, yr, off);
 }
 
 // Streaming kernel for int8 layers with a short reduction: R x S taps of CS
-// k-steps (64 channels each).  Persistent: one workgroup per CU.  Each wave
-// keeps its 64-channel slice of the packed filter in registers for the whole
-// kernel (no LDS traffic) and walks a contiguous range of 16-pixel tiles;
-// workgroup ranges are grouped by XCD so neighbouring tiles, which share
-// input rows, share an L2.  Per tile, the patch fragments of all k-steps are
-// buffer loads issued two tiles ahead; a tap outside the image gets an
-// offset past the extent and reads zeros.  Each iteration issues the current
-// tile's MFMAs and, in the same basic block, the previous tile's epilogue,
-// so the matrix cores and the VALU work overlap.  Offsets use 24-bit
+// k-steps (64 channels each).  Persistent: one workgroup per CU of 4 "pixel
+// waves", each walking every 4th 16-pixel tile of the workgroup's range.
+// With KSPLIT = 2 a pixel wave is a pair of waves that split the 64-channel
+// filter slice (32 channels and 8 outputs per lane each, two waves per
+// SIMD); with KSPLIT = 1 one wave holds all 64 channels (16 outputs per
+// lane, one wave per SIMD).  The filter slice stays in registers for the
+// whole kernel.  Workgroup ranges are grouped by XCD so neighbouring tiles,
+// which share input rows, share an L2.  Per tile, the patch fragments of all
+// k-steps are buffer loads issued two tiles ahead; a tap outside the image
+// gets an offset past the extent and reads zeros.  Offsets use 24-bit
 // multiplies (every operand and product here is far below 2^24 / 2^31).
-template <int R, int S, int CS, bool SIDE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int R, int S, int CS, bool SIDE, int KSPLIT>
+__global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(KSPLIT, KSPLIT)))
 void conv_stream_i8_kernel(ConvArgs a) {
   constexpr int NKS = R * S * CS;
+  constexpr int NOUT = 16 / KSPLIT;  // outputs (channels) per lane
+  constexpr int NJ = 4 / KSPLIT;     // 16-row MFMA tiles per wave
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kh = wave % KSPLIT;  // which channels of the slice
+  const int pw = wave / KSPLIT;  // tiles pw, pw + 4, ... of the workgroup's range
   const int g = lane >> 4;
   const int col = lane & 15;
-  const int ch0 = blockIdx.y * 64 + 16 * g;
+  const int ch0 = blockIdx.y * 64 + 16 * g + NOUT * kh;  // this lane's NOUT channels
 
   const int G = gridDim.x;
   const int bx = blockIdx.x;
   const int b = (G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
   const int t_begin = b * a.tiles / G;  // b * tiles < 2^31 (checked at plan time)
   const int t_end = (b + 1) * a.tiles / G;
-  const int n_tiles = t_end - t_begin - wave > 0 ? (t_end - t_begin - wave + 3) / 4 : 0;
+  const int n_tiles = t_end - t_begin - pw > 0 ? (t_end - t_begin - pw + 3) / 4 : 0;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
@@ -821,9 +919,9 @@ void conv_stream_i8_kernel(ConvArgs a) {
       for (int c = 0; c < CS; ++c) delta[(r * S + s) * CS + c] = r * WCB + s * CB + c * 64;
 
   // Buffer offsets of tile k's patch fragments (past the extent when the tap
-  // falls outside the image or the tile outside this wave's range).
+  // falls outside the image or the tile outside this pair's range).
   auto offsets = [&](int k, uint32_t(&o)[NKS]) {
-    const int t = t_begin + wave + 4 * k;
+    const int t = t_begin + pw + 4 * k;
     const uint32_t m = static_cast<uint32_t>(t * 16 + col);
     const bool live = static_cast<unsigned>(k) < static_cast<unsigned>(n_tiles) &&
                       m < static_cast<uint32_t>(a.M);
@@ -858,16 +956,19 @@ void conv_stream_i8_kernel(ConvArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) f[ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, o[ks], 0, 0);
   };
-  // Output (and side-input) offset of tile k for this lane, or out of range;
-  // the uniform range test is folded into one unsigned compare.
+  // Output (and side-input) offset of tile k for this lane, or out of range.
   auto out_off = [&](int k) -> uint32_t {
-    const int m = (t_begin + wave + 4 * k) * 16 + col;
+    const int m = (t_begin + pw + 4 * k) * 16 + col;
     const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(n_tiles) &&
                     m < a.M && ch0 < a.K;
     return ok ? static_cast<uint32_t>(__mul24(m, a.K) + ch0) : kOutOfRange;
   };
   auto issue_side = [&](int k) -> i32x4 {
-    if constexpr (SIDE) return __builtin_amdgcn_raw_buffer_load_b128(sr, out_off(k), 0, 0);
+    if constexpr (SIDE) {
+      if constexpr (NOUT == 16) return __builtin_amdgcn_raw_buffer_load_b128(sr, out_off(k), 0, 0);
+      const i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(sr, out_off(k), 0, 0);
+      return i32x4{v.x, v.y, 0, 0};
+    }
     return i32x4{0, 0, 0, 0};
   };
 
@@ -881,22 +982,21 @@ void conv_stream_i8_kernel(ConvArgs a) {
   i32x4 sA = issue_side(0);
 
   // The 64-channel filter slice crosses L2 once per workgroup: a direct
-  // global->LDS copy of its 64 padded rows, then every wave reads its
-  // fragments for all k-steps and the 4 MFMA tiles into registers.  The 16
-  // bias values of this lane's channels come in with four buffer loads
-  // (channels past K read 0).
+  // global->LDS copy of its 64 padded rows, then every wave reads the
+  // fragments of its rows for all k-steps into registers.  The bias of this
+  // lane's channels comes in with buffer loads (channels past K read 0).
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int RS = a.wrow_bytes;
   {
     const char* src = static_cast<const char*>(a.wp) + static_cast<int64_t>(blockIdx.y) * 64 * RS;
-    for (int i = wave; i < RS / 16; i += 4)
+    for (int i = wave; i < RS / 16; i += 4 * KSPLIT)
       __builtin_amdgcn_global_load_lds(src + i * 1024 + lane * 16,
                                        (lds_ptr_t)(smem + i * 1024), 16, 0, 0);
   }
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, static_cast<uint32_t>(a.K) * 4u);
-  float bias[16];
+  float bias[NOUT];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NOUT / 4; ++q) {
     const f32x4 v = __builtin_bit_cast(
         f32x4, __builtin_amdgcn_raw_buffer_load_b128(br, static_cast<uint32_t>((ch0 + 4 * q) * 4), 0, 0));
     bias[4 * q] = v.x;
@@ -908,67 +1008,52 @@ void conv_stream_i8_kernel(ConvArgs a) {
   const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
   __syncthreads();
-  i32x4 Wf[NKS][4];
+  i32x4 Wf[NKS][NJ];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      Wf[ks][j] = *reinterpret_cast<const i32x4*>(smem + (j * 16 + col) * RS + ks * 64 + g * 16);
+    for (int j = 0; j < NJ; ++j)
+      Wf[ks][j] = *reinterpret_cast<const i32x4*>(smem + ((NJ * kh + j) * 16 + col) * RS +
+                                                  ks * 64 + g * 16);
 
-  i32x4 accA[4], accB[4];
+  i32x4 accA[NJ], accB[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) accB[j] = zero4;
+  for (int j = 0; j < NJ; ++j) accB[j] = zero4;
 
   // One half of a loop trip, software-pipelined by hand: the MFMAs of the
   // tile in bX (into accX) are split by k-step into NKS chunks; each chunk
-  // also issues that k-step's refill load for tile k_load and finishes EPC of
-  // the 16 epilogue outputs of the previous tile (accY, side sY).  A
-  // scheduling barrier closes each chunk, so the VALU epilogue runs under the
-  // matrix-core work instead of before or after it.
-  constexpr int EPC = (16 + NKS - 1) / NKS;
-  auto half = [&](i32x4(&bX)[NKS], i32x4(&accX)[4], const i32x4(&accY)[4], i32x4 sY,
+  // also issues that k-step's refill load for tile k_load and runs its share
+  // of the epilogue stages of the previous tile (accY, side sY).  A
+  // scheduling barrier closes each chunk.
+  auto half = [&](i32x4(&bX)[NKS], i32x4(&accX)[NJ], const i32x4(&accY)[NJ], i32x4 sY,
                   int k_load, uint32_t off_prev) {
     uint32_t o[NKS];
     offsets(k_load, o);
-    union {
-      int8_t b[16];
-      i32x4 v;
-    } sd;
-    sd.v = sY;
-    uint32_t pairs[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    EpiI8<SIDE, NOUT> ep;
+#pragma unroll
+    for (int j = 0; j < NOUT / 4; ++j) ep.w[j] = 0u;
+    constexpr int NS = EpiI8<SIDE, NOUT>::kStages;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         accX[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Wf[ks][j], bX[ks],
                                                         ks == 0 ? zero4 : accX[j], 0, 0, 0);
       bX[ks] = __builtin_amdgcn_raw_buffer_load_b128(xr, o[ks], 0, 0);
-      // EPC is even, so a chunk finishes whole pairs of outputs.
+      // Epilogue stages [ceil(ks*NS/NKS), ceil((ks+1)*NS/NKS)) in this chunk.
 #pragma unroll
-      for (int e = ks * EPC; e < (ks + 1) * EPC && e < 16; e += 2) {
-        const uint32_t v0 = requant_i8_bits<SIDE>(accY[e / 4][e % 4], sd.b[e], bias[e], cis,
-                                                  sis, lo_b, hi_b);
-        const uint32_t v1 = requant_i8_bits<SIDE>(accY[e / 4][e % 4 + 1], sd.b[e + 1],
-                                                  bias[e + 1], cis, sis, lo_b, hi_b);
-        pairs[e / 2] = pack_pair(v0, v1);
-        if (e % 4 == 2) words[e / 4] = pack_word(pairs[e / 2 - 1], pairs[e / 2]);
-      }
-      // Pin this chunk's outputs here: without it the arithmetic, which has
-      // no memory effects, is sunk to the store at the end of the half.
-      asm volatile("" : "+v"(words[0]), "+v"(words[1]), "+v"(words[2]), "+v"(words[3]),
-                   "+v"(pairs[0]), "+v"(pairs[2]), "+v"(pairs[4]), "+v"(pairs[6]));
+      for (int st = (ks * NS + NKS - 1) / NKS; st < ((ks + 1) * NS + NKS - 1) / NKS; ++st)
+        ep.stage(st, accY, sY, bias, cis, sis, lo_b, hi_b);
+      ep.pin();
+      interleave_mfma_valu<NJ>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_raw_buffer_store_b128(
-        i32x4{static_cast<int32_t>(words[0]), static_cast<int32_t>(words[1]),
-              static_cast<int32_t>(words[2]), static_cast<int32_t>(words[3])},
-        yr, off_prev, 0, 0);
+    store_words<NOUT>(ep.w, yr, off_prev);
   };
 
   // Two tiles per trip and no exit in between, so both halves see the same
   // memory-operation history: half A computes tile k and finishes tile k-1,
-  // half B computes tile k+1 and finishes tile k.  A tile past the wave's
+  // half B computes tile k+1 and finishes tile k.  A tile past the pair's
   // range loads zeros and its store is dropped.
   int k = 0;
   for (; k < n_tiles; k += 2) {
@@ -977,7 +1062,315 @@ void conv_stream_i8_kernel(ConvArgs a) {
     half(bB, accB, accA, sA, k + 3, out_off(k));
     sA = issue_side(k + 2);
   }
-  stream_epilogue_i8<SIDE>(accB, sB, bias, cis, sis, lo_b, hi_b, yr, out_off(k - 1));
+  stream_epilogue_i8<SIDE, NOUT>(accB, sB, bias, cis, sis, lo_b, hi_b, yr, out_off(k - 1));
+}
+
+// ------------------------------------------------------------- row-halo int8
+//
+// Stride-1 int8 convolution over 64 input channels (one 64-byte k-step per
+// filter tap) for short reductions such as 3x3x64.  A workgroup owns
+// `halo_rows` consecutive output rows (flattened n*Ho + ho) and one 64-channel
+// slice of the filter, split into two phases of rows.  At start it issues
+// every load it will need as buffer->LDS copies: the filter slice, then for
+// each phase each distinct input row of the phase's footprint (zero rows and
+// zero columns for the padding come from out-of-range buffer offsets, which
+// read as zero) and the phase's side-input tile.  Phase A's data lands first;
+// its tiles are computed while phase B's copies are still in flight (each
+// phase stages into its own LDS arrays, so reading one does not wait for
+// copies into the other).  B fragments are read from LDS, so no tile waits on
+// device memory.
+//
+// Each input row lives in a 4 KiB slot: pixel X (halo column, X = input
+// column + left pad) holds its four 16-byte channel chunks at positions
+// 4X + (c ^ ((X >> 1) & 3)); with that swizzle a wave reading 16 consecutive
+// pixels x one chunk per lane group runs at the contention-free ds_read_b128
+// rate for any starting pixel.  The side tile uses the same swizzle over the
+// phase's pixel index.  Slot of tap row r for phase row j of image n:
+// j + r + (R-1)*(n - n0), n0 = the phase's first image; consecutive output
+// rows of one image share R-1 input rows, and each image change skips R-1
+// slots so that rows of different images never collide.
+//
+// Four pixel waves walk every 4th 16-pixel tile of a phase; each is a pair
+// of waves that split the 64 channels (32 each, 8 outputs per lane), two
+// waves per SIMD, so one wave's requantisation VALU work runs while the
+// other's MFMAs occupy the matrix core.
+constexpr int kHaloSlot = 4096;
+constexpr int kHaloSlots = 7;       // input-row slots per phase
+constexpr int kHaloSidePx = 256;    // side-tile pixels per phase
+constexpr int kHaloThreads = 512;
+
+__device__ inline uint32_t halo_pos(int x, int c) {
+  return static_cast<uint32_t>(4 * x + (c ^ ((x >> 1) & 3)));
+}
+
+// Rows [p0, p1) of one phase.
+struct HaloPhase {
+  int p0, p1, n0, ho0, nslots, npx, ntile;
+};
+
+__device__ inline HaloPhase halo_phase(const ConvArgs& a, int p0, int p1, int R) {
+  HaloPhase h;
+  h.p0 = p0;
+  h.p1 = p1;
+  if (p1 <= p0) {
+    h.n0 = h.ho0 = h.nslots = h.npx = h.ntile = 0;
+    return h;
+  }
+  h.n0 = static_cast<int>(fast_div(static_cast<uint32_t>(p0), a.ho_mul, a.ho_add, a.ho_shift));
+  const int n_last =
+      static_cast<int>(fast_div(static_cast<uint32_t>(p1 - 1), a.ho_mul, a.ho_add, a.ho_shift));
+  h.ho0 = p0 - h.n0 * a.Ho;
+  h.nslots = (p1 - p0) + (R - 1) * (n_last - h.n0 + 1);
+  h.npx = (p1 - p0) * a.Wo;
+  h.ntile = (h.npx + 15) >> 4;
+  return h;
+}
+
+// s_waitcnt with vmcnt = min(n, 15) (expcnt and lgkmcnt not waited on).
+// Waiting with a smaller count than needed is always safe.
+__device__ inline void wait_vmcnt_at_most(int n) {
+  switch (n < 15 ? n : 15) {
+#define FCONV_VMWAIT(k) \
+  case k:               \
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (k));  \
+    break;
+    FCONV_VMWAIT(0) FCONV_VMWAIT(1) FCONV_VMWAIT(2) FCONV_VMWAIT(3) FCONV_VMWAIT(4)
+    FCONV_VMWAIT(5) FCONV_VMWAIT(6) FCONV_VMWAIT(7) FCONV_VMWAIT(8) FCONV_VMWAIT(9)
+    FCONV_VMWAIT(10) FCONV_VMWAIT(11) FCONV_VMWAIT(12) FCONV_VMWAIT(13) FCONV_VMWAIT(14)
+    default:
+      __builtin_amdgcn_s_waitcnt(0x0f70 | 15);
+      break;
+#undef FCONV_VMWAIT
+  }
+}
+
+template <int R, int S, bool SIDE>
+__global__ __launch_bounds__(kHaloThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void conv_halo_i8_kernel(ConvArgs a) {
+  constexpr int NKS = R * S;
+  constexpr int RSB = NKS * 64 + 16;  // packed filter row bytes
+  __shared__ __attribute__((aligned(16))) char wlds[64 * RSB];
+  __shared__ __attribute__((aligned(256))) char xa[kHaloSlots * kHaloSlot];
+  __shared__ __attribute__((aligned(256))) char xb[kHaloSlots * kHaloSlot];
+  __shared__ __attribute__((aligned(256))) char sa[SIDE ? kHaloSidePx * 64 : 16];
+  __shared__ __attribute__((aligned(256))) char sb[SIDE ? kHaloSidePx * 64 : 16];
+  // Accumulator hand-off, per MFMA wave and step parity: chunk q (accumulator
+  // tile q, 4 int32) of lane l at q * 1024 + 16 * l.
+  __shared__ __attribute__((aligned(256))) char accb[4 * 2 * 4096];
+  __shared__ __attribute__((aligned(16))) float blds[256];  // the slice's 64 bias values
+
+  const int lane = threadIdx.x & 63;
+  // readfirstlane: the wave index (and so the role) is uniform per wave.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool mfma_role = wave < 4;  // waves 0-3 MFMA, 4-7 epilogue (same SIMDs)
+  const int m = wave & 3;           // tiles m, m + 4, ... of each phase
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int ch0 = blockIdx.y * 64 + 16 * g;
+
+  const int G = gridDim.x;
+  const int bx = blockIdx.x;
+  const int b = (G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
+  const int rows_total = a.N * a.Ho;
+  const int g0 = b * a.halo_rows;
+  if (g0 >= rows_total) return;  // uniform per workgroup
+  const int g1 = min(g0 + a.halo_rows, rows_total);
+  const int gm = min(g0 + a.halo_rows_a, g1);
+  const HaloPhase PA = halo_phase(a, g0, gm, R);
+  const HaloPhase PB = halo_phase(a, gm, g1, R);
+  const int sA = (PA.ntile + 3) >> 2;  // steps of each phase (4 tiles per step)
+  const int sB = (PB.ntile + 3) >> 2;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, static_cast<uint32_t>(a.K) * 4u);
+
+  // ---- buffer->LDS copies of 1 KiB.  Nothing is loaded into registers:
+  // a register load issued among the copies could only be waited for together
+  // with all of them.
+  auto copy_rows = [&](const HaloPhase& P, char* xbuf, int k) {
+    const int sigma = k >> 2;
+    // image segment e holding slot sigma: phase rows [js, je) of image n0+e
+    // own slots [js + (R-1)e, je + (R-1)(e+1)).
+    int e = 0, js = 0;
+    int je = min(P.p1 - P.p0, a.Ho - P.ho0);
+    while (sigma >= je + (R - 1) * (e + 1)) {
+      ++e;
+      js = je;
+      je = min(P.p1 - P.p0, je + a.Ho);
+    }
+    const int n = P.n0 + e;
+    const int hi = (e == 0 ? P.ho0 : 0) - a.pt + (sigma - js - (R - 1) * e);
+    const int pos = (k & 3) * 64 + lane;  // position inside the 4 KiB slot
+    const int X = pos >> 2;
+    const int c = (pos & 3) ^ ((X >> 1) & 3);
+    const int wi = X - a.pl;
+    const bool ok = static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                    static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+    const uint32_t src = ok ? static_cast<uint32_t>(((n * a.H + hi) * a.W + wi) * 64 + c * 16)
+                            : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xr, (lds_ptr_t)(xbuf + sigma * kHaloSlot + (k & 3) * 1024), 16, src, 0, 0, 0);
+  };
+  auto copy_side = [&](const HaloPhase& P, char* sbuf, int k) {
+    const int pos = k * 64 + lane;
+    const int pp = pos >> 2;
+    const int c = (pos & 3) ^ ((pp >> 1) & 3);
+    const int ch = blockIdx.y * 64 + 16 * c;
+    const bool ok = pp < P.npx && ch < a.K;
+    const uint32_t src =
+        ok ? static_cast<uint32_t>((P.p0 * a.Wo + pp) * a.K + ch) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(sbuf + k * 1024), 16, src, 0, 0, 0);
+  };
+
+  if (mfma_role) {
+    // MFMA waves copy, in this order: filter slice, phase A rows, phase B
+    // rows, phase B side tile; they then wait for all but their phase-B
+    // copies.  They issue no stores, so a later wait for the phase-B copies
+    // never waits for output writes.
+    const int n_filter = RSB / 16;  // 64 rows of RSB bytes = RSB/16 KiB
+    const int e1 = n_filter, e2 = e1 + 4 * PA.nslots, e3 = e2 + 4 * PB.nslots;
+    const int e4 = e3 + (SIDE ? PB.ntile : 0);
+    for (int i = m; i < e4; i += 4) {
+      if (i < e1) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (lds_ptr_t)(wlds + i * 1024), 16,
+            static_cast<uint32_t>(blockIdx.y * 64 * RSB + i * 1024 + lane * 16), 0, 0, 0);
+      } else if (i < e2) {
+        copy_rows(PA, xa, i - e1);
+      } else if (i < e3) {
+        copy_rows(PB, xb, i - e2);
+      } else {
+        copy_side(PB, sb, i - e3);
+      }
+    }
+    const int first_b = e2 + ((m - e2) % 4 + 4) % 4;  // first index >= e2 with i % 4 == m
+    wait_vmcnt_at_most(first_b < e4 ? (e4 - first_b + 3) / 4 : 0);
+  } else {
+    // Epilogue waves copy the bias and the phase A side tile.
+    const int e1 = 1, e2 = e1 + (SIDE ? PA.ntile : 0);
+    for (int i = m; i < e2; i += 4) {
+      if (i == 0) {
+        const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
+                                       : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
+      } else {
+        copy_side(PA, sa, i - e1);
+      }
+    }
+  }
+  // Every wave has waited for the copies the next step reads before it
+  // arrives, and LDS has no cache, so a plain s_barrier publishes them.
+  // (__syncthreads() would add a release fence, which waits for every
+  // outstanding copy.)
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  barrier();
+
+  if (mfma_role) {
+    i32x4 Wf[NKS][4];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        Wf[ks][j] = *reinterpret_cast<const i32x4*>(wlds + (j * 16 + col) * RSB + ks * 64 + g * 16);
+    const i32x4 zero4 = i32x4{0, 0, 0, 0};
+
+    // One phase of MFMA steps.  Step ls computes tile m + 4*ls (lanes past
+    // the phase's pixels read the last pixel; their results are never
+    // stored) and hands its accumulators to the epilogue wave of this SIMD.
+    auto mfma_phase = [&](const HaloPhase& P, const char* xbuf, int steps, int step0, bool last) {
+      if (steps == 0) return;
+      // LDS addresses of the tile of step ls for this lane: tap (r, s) is
+      // ad[s] + r * kHaloSlot.
+      auto tile_addr = [&](int ls, uint32_t(&ad)[S]) {
+        const int p = min((m + 4 * ls) * 16 + col, P.npx - 1);
+        const int j = static_cast<int>(fast_div(static_cast<uint32_t>(p), a.wo_mul, a.wo_add, a.wo_shift));
+        const int wo = p - j * a.Wo;
+        const int n = static_cast<int>(fast_div(static_cast<uint32_t>(P.p0 + j), a.ho_mul, a.ho_add, a.ho_shift));
+        const uint32_t base = static_cast<uint32_t>((j + (R - 1) * (n - P.n0)) * kHaloSlot);
+#pragma unroll
+        for (int s = 0; s < S; ++s) ad[s] = base + 16u * halo_pos(wo + s, g);
+      };
+      auto frag = [&](uint32_t addr) -> i32x4 {
+        return *reinterpret_cast<const i32x4*>(xbuf + addr);
+      };
+      i32x4 bf[NKS];
+      {
+        uint32_t ad[S];
+        tile_addr(0, ad);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) bf[ks] = frag(ad[ks % S] + (ks / S) * kHaloSlot);
+      }
+      for (int ls = 0; ls < steps; ++ls) {
+        // The next step's fragments are refilled k-step by k-step as soon
+        // as this step's MFMAs have consumed them.
+        uint32_t ad[S];
+        tile_addr(ls + 1 < steps ? ls + 1 : ls, ad);
+        i32x4 acc[4];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Wf[ks][j], bf[ks],
+                                                           ks == 0 ? zero4 : acc[j], 0, 0, 0);
+          bf[ks] = frag(ad[ks % S] + (ks / S) * kHaloSlot);
+        }
+        // Keep each refill next to its k-step's MFMAs so that its latency
+        // hides under the remaining ones (left alone, the scheduler moves
+        // every read to the end of the step).
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        char* dst = accb + (m * 2 + ((step0 + ls) & 1)) * 4096 + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<i32x4*>(dst + j * 1024) = acc[j];
+        if (last && ls + 1 == steps) __builtin_amdgcn_s_waitcnt(0);  // this wave's phase-B copies
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
+        barrier();
+      }
+    };
+    mfma_phase(PA, xa, sA, 0, true);
+    mfma_phase(PB, xb, sB, sA, false);
+    barrier();  // the epilogue waves' last step
+  } else {
+    // Step 0 (the MFMA waves compute the first tiles): wait for this wave's
+    // copies (bias, phase A side tile) before the barrier that publishes
+    // them to the other epilogue waves; no output has been stored yet, so
+    // this waits for nothing else.
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier();
+    float bias[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bias[e] = blds[16 * g + e];
+    const float cis = a.cis, sis = a.sis;
+    const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
+    auto epi_phase = [&](const HaloPhase& P, const char* sbuf, int steps, int step0) {
+      for (int ls = 0; ls < steps; ++ls) {
+        const char* src = accb + (m * 2 + ((step0 + ls) & 1)) * 4096 + 16 * lane;
+        i32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = *reinterpret_cast<const i32x4*>(src + j * 1024);
+        const int p = (m + 4 * ls) * 16 + col;
+        i32x4 sd = i32x4{0, 0, 0, 0};
+        if constexpr (SIDE)
+          sd = *reinterpret_cast<const i32x4*>(sbuf + 16u * halo_pos(min(p, P.npx - 1), g));
+        const bool ok = p < P.npx && ch0 < a.K;
+        const uint32_t off = ok ? static_cast<uint32_t>((P.p0 * a.Wo + p) * a.K + ch0) : kOutOfRange;
+        stream_epilogue_i8<SIDE, 16>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
+        barrier();
+      }
+    };
+    epi_phase(PA, sa, sA, 0);
+    epi_phase(PB, sb, sB, sA);
+  }
 }
 
 // ------------------------------------------------------------- dispatch
@@ -1061,9 +1454,9 @@ hipError_t launch_stream_shape(const fconv_plan_s* p, const ConvArgs& a, hipStre
   const dim3 g(static_cast<unsigned>(grid), static_cast<unsigned>(p->Kp / 64));
   const size_t lds = static_cast<size_t>(64) * a.wrow_bytes;
   if (a.use_side)
-    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true>), g, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true, 1>), g, dim3(kThreads), lds, s, a);
   else
-    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false>), g, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false, 1>), g, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1079,6 +1472,54 @@ hipError_t launch_stream(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s
       default: break;
     }
   }
+  return hipErrorInvalidValue;
+}
+
+// Whether every phase of the row-halo kernel fits its LDS arrays when each
+// workgroup takes `rows` output rows (the first ceil(rows/2) in phase A):
+// input-row slots (rows + (R-1) per image the phase touches) and side
+// pixels, checked exactly for every workgroup.
+bool halo_fits(const fconv_plan_s* p, int rows) {
+  const int64_t rows_total = static_cast<int64_t>(p->d.N) * p->Ho;
+  const int ra = (rows + 1) / 2;
+  if (static_cast<int64_t>(ra) * p->Wo > kHaloSidePx) return false;
+  for (int64_t g0 = 0; g0 < rows_total; g0 += rows) {
+    const int64_t g1 = std::min<int64_t>(g0 + rows, rows_total);
+    const int64_t gm = std::min<int64_t>(g0 + ra, g1);
+    const int64_t bounds[3] = {g0, gm, g1};
+    for (int ph = 0; ph < 2; ++ph) {
+      const int64_t p0 = bounds[ph], p1 = bounds[ph + 1];
+      if (p1 <= p0) continue;
+      const int64_t images = (p1 - 1) / p->Ho - p0 / p->Ho + 1;
+      if ((p1 - p0) + (p->d.R - 1) * images > kHaloSlots) return false;
+    }
+  }
+  return true;
+}
+
+template <int R, int S>
+hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStream_t s) {
+  ConvArgs a = a0;
+  const int cus = device_cu_count();
+  const int rows_total = p->d.N * p->Ho;
+  int rows = p->halo_rows > 0 ? std::min(p->halo_rows, rows_total)
+                              : (rows_total + cus - 1) / cus;
+  // Two phases of ceil(rows/2) and floor(rows/2) rows, each within one
+  // phase's LDS arrays.
+  while (rows > 1 && !halo_fits(p, rows)) --rows;
+  if (!halo_fits(p, rows)) return hipErrorInvalidValue;
+  a.halo_rows = rows;
+  a.halo_rows_a = (rows + 1) / 2;
+  const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows), static_cast<unsigned>(p->Kp / 64));
+  if (a.use_side)
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true>), g, dim3(kHaloThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false>), g, dim3(kHaloThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_halo(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  if (p->d.R == 3 && p->d.S == 3) return launch_halo_shape<3, 3>(p, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -1100,6 +1541,7 @@ hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
 
 hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
   if (p->variant == kStream) return launch_stream(p, a, s);
+  if (p->variant == kHalo) return launch_halo(p, a, s);
   if (p->variant == kTiled) {
     switch (p->d.dtype) {
       case FCONV_INT8: return launch_tile<FCONV_INT8>(p, a, s);

@@ -74,11 +74,12 @@ fconv_status parse_ops(fconv_plan_s* p) {
 }
 
 const char* kernel_name(int32_t variant, int32_t dtype) {
-  static const char* names[4][3] = {
+  static const char* names[5][3] = {
       {"conv_general_i8", "conv_general_bf16", "conv_general_f32"},
       {"conv_rf_i8", "conv_rf_bf16", "conv_rf_f32"},
       {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"},
-      {"conv_tile_i8", "conv_tile_bf16", "conv_tile_f32"}};
+      {"conv_tile_i8", "conv_tile_bf16", "conv_tile_f32"},
+      {"conv_halo_i8", "conv_halo_bf16", "conv_halo_f32"}};
   return names[variant][dtype];
 }
 
@@ -86,13 +87,16 @@ const char* kernel_name(int32_t variant, int32_t dtype) {
 // this much, so that two workgroups still fit in a CU's 160 KiB.
 constexpr int64_t kRfMaxLds = 80 * 1024;
 
-// Kernel choice.  FCONV_FORCE_VARIANT=general (environment) pins the general
-// kernel, for A/B comparisons; FCONV_RF_PT=1|2|4 overrides the pixel tiles.
+// Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream (environment)
+// pins a kernel family where the shape allows it, for A/B comparisons;
+// FCONV_RF_PT=1|2|4 overrides the pixel tiles, FCONV_HALO_ROWS the output rows
+// per workgroup of the row-halo kernel.
 void choose_variant(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
   p->variant = kGeneral;
   p->pixel_tiles = 1;
   p->ring_depth = 0;
+  p->halo_rows = 0;
   const int64_t rf_lds = 64 * static_cast<int64_t>(p->wrow_bytes);
   const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
   const char* force = getenv("FCONV_FORCE_VARIANT");
@@ -139,6 +143,16 @@ void choose_variant(fconv_plan_s* p) {
     const int64_t tiles = (p->M + 15) / 16;
     if (!rf_only && d.dtype == FCONV_INT8 && shape_ok && tiles * 1024 < (int64_t{1} << 31))
       p->variant = kStream;
+    // Stride 1, 3x3 over 64 channels, padded input rows of at most 64 pixels
+    // (one 4 KiB LDS slot each): the row-halo kernel, unless the streaming
+    // kernel is asked for by name.
+    const bool force_stream = force && strcmp(force, "stream") == 0;
+    if (p->variant == kStream && !force_stream && d.R == 3 && d.S == 3 && cs == 1 &&
+        d.stride_h == 1 && d.stride_w == 1 && d.W + p->pl + p->pr <= 64) {
+      p->variant = kHalo;
+      const char* hr = getenv("FCONV_HALO_ROWS");
+      if (hr && atoi(hr) > 0) p->halo_rows = atoi(hr);
+    }
   }
   p->kernel_name = kernel_name(p->variant, d.dtype);
 }

@@ -16,6 +16,7 @@ enum Variant : int32_t {
   kResidentFilter = 1, // 64-channel filter slice staged in LDS once per workgroup
   kStream = 2,         // int8, short reduction: filter in registers, persistent
   kTiled = 3,          // 128x128 LDS-tiled implicit GEMM, long reductions
+  kHalo = 4,           // int8 stride 1 over 64 channels: input rows staged in LDS
 };
 
 // Division by a runtime constant d for numerators below 2^31:
@@ -50,6 +51,7 @@ struct fconv_plan_s {
   int32_t variant;
   int32_t pixel_tiles;  // kResidentFilter: 16-pixel MFMA tiles per wave (1, 2, 4)
   int32_t ring_depth;   // kResidentFilter: k-steps of patch loads in flight
+  int32_t halo_rows;    // kHalo: output rows per workgroup, 0 = sized to the device
   int32_t wrow_bytes;   // packed filter row stride: KgP * esize + 16 (zero pad)
   fconv::FastDiv wo_div, ho_div;
   size_t ws_bytes;      // packed filter: Kp * wrow_bytes

@@ -250,8 +250,43 @@ def test_pack_filter_then_prepacked_run_matches():
         assert np.array_equal(a, b), dtype
 
 
+@pytest.mark.parametrize("N,H,W,K,pad,side,rows", [
+    (5, 7, 9, 64, "SAME", True, 0),      # one output row per workgroup
+    (3, 1, 1, 64, "SAME", True, 0),      # 1x1 images: all but the centre tap in padding
+    (2, 13, 62, 128, "SAME", True, 0),   # widest padded row (64 pixels), two channel slices
+    (7, 5, 6, 80, "VALID", True, 0),     # K not a multiple of 64, VALID
+    (1, 3, 3, 16, "SAME", False, 0),     # K = 16, no side input
+    (100, 5, 5, 64, "SAME", True, 0),    # several rows per workgroup, rows span images
+    (300, 3, 3, 64, "SAME", True, 0),    # workgroups span up to three images
+    (600, 1, 8, 64, "SAME", True, 0),    # one-row images: every workgroup row is a new image
+    (2, 3, 20, 64, "VALID", True, 0),    # Ho = 1 with VALID padding
+    (6, 9, 11, 64, "SAME", True, 5),     # forced 5 rows per workgroup
+    (4, 16, 16, 64, "SAME", True, 13),   # forced 13 rows: ragged last workgroup
+])
+def test_halo_shapes(N, H, W, K, pad, side, rows, monkeypatch):
+    """Row-halo kernel edge cases: padding rows and columns, image changes
+    inside a workgroup's rows, ragged pixel and channel tails."""
+    if rows:
+        monkeypatch.setenv("FCONV_HALO_ROWS", str(rows))
+    rng = np.random.default_rng(N * 1000 + H * 10 + K)
+    Ho, Wo = oracle.geometry(H, W, 3, 3, 1, 1, pad == "SAME")[:2]
+    x = wl.draw_int8(rng, (N, H, W, 64), -128, 127)
+    w = wl.draw_int8(rng, (3, 3, 64, K), -128, 127)
+    sd = wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if side else None
+    ops = [wl.OP_SCALE] + ([wl.OP_SIDE] if side else []) + [wl.OP_BIAS, wl.OP_RELU]
+    c = dict(shape=(N, H, W, 64, K, 3, 3, 1, pad), x=x, w=w,
+             bias=rng.normal(0, 40, K).astype(np.float32), side=sd,
+             cis=np.float32(2.0 ** -10), sis=np.float32(0.5 if side else 0.0), relu=True,
+             ops=ops, bn=None, use_bias=True)
+    say("halo shape %s side=%s rows=%d" % (c["shape"], side, rows))
+    y, r, guards, plan = _run_case(c, "int8")
+    assert plan.kernel_name == "conv_halo_i8", plan.kernel_name
+    assert guards
+    assert np.array_equal(y, r), "%d differ" % np.count_nonzero(y != r)
+
+
 @pytest.mark.parametrize("name,variant", [
-    ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"),
+    ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"), ("resnet_3x3_int8", "stream"),
     ("resnet_1x1_int8", "general"), ("resnet_1x1_int8", "rf"), ("resnet_1x1_int8", "tile"),
     ("resnet_3x3s2_int8", "general"), ("resnet_3x3s2_int8", "rf")])
 def test_workload_forced_variant(name, variant, monkeypatch):
