@@ -166,23 +166,31 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Side-input chunk of output pixel m, channels ch0 .. ch0+15 (zero past K).
+// Side-input chunk of output pixel m, channels ch0 .. ch0+NCH-1 (zero past
+// K), NCH = 16 or 8 (then in the low 8 bytes).
+template <int NCH = 16>
 __device__ inline i32x4 load_side_chunk(const ConvArgs& a, int m, int ch0, bool kvec) {
   const int8_t* side = a.side + static_cast<int64_t>(m) * a.K + ch0;
-  if (kvec) return *reinterpret_cast<const i32x4*>(side);
+  if (kvec) {
+    if constexpr (NCH == 16) return *reinterpret_cast<const i32x4*>(side);
+    const i32x2 v = *reinterpret_cast<const i32x2*>(side);
+    return i32x4{v.x, v.y, 0, 0};
+  }
   union {
     int8_t b[16];
     i32x4 v;
   } s;
+  s.v = i32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s.b[e] = (ch0 + e < a.K) ? side[e] : int8_t(0);
+  for (int e = 0; e < NCH; ++e) s.b[e] = (ch0 + e < a.K) ? side[e] : int8_t(0);
   return s.v;
 }
 
 // int8: TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel (cuDNN 8
 // order).  v[e] is the int32 accumulator of channel ch0 + e; side_chunk holds
-// the int8 side input of the same 16 channels (ignored unless a.use_side).
-__device__ inline void epilogue_store_i8(const int32_t (&v)[16], const ConvArgs& a,
+// the int8 side input of the same NCH channels (ignored unless a.use_side).
+template <int NCH = 16>
+__device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs& a,
                                          int m, int ch0, bool kvec, i32x4 side_chunk) {
   int8_t* y = static_cast<int8_t*>(a.y) + static_cast<int64_t>(m) * a.K + ch0;
   union {
@@ -190,9 +198,10 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[16], const ConvArgs&
     i32x4 v;
   } s, o;
   s.v = side_chunk;
+  o.v = i32x4{0, 0, 0, 0};
   const float lo = a.relu ? 0.0f : -128.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < NCH; ++e) {
     const int ch = ch0 + e;
     const float b = (kvec || ch < a.K) ? a.bias[ch] : 0.0f;
     float t = static_cast<float>(v[e]);        // int32 -> fp32, nearest even
@@ -204,21 +213,24 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[16], const ConvArgs&
     o.b[e] = static_cast<int8_t>(static_cast<int32_t>(t));
   }
   if (kvec) {
-    *reinterpret_cast<i32x4*>(y) = o.v;
+    if constexpr (NCH == 16)
+      *reinterpret_cast<i32x4*>(y) = o.v;
+    else
+      *reinterpret_cast<i32x2*>(y) = i32x2{o.v.x, o.v.y};
   } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+    for (int e = 0; e < NCH; ++e)
       if (ch0 + e < a.K) y[e] = o.b[e];
   }
 }
 
 // bf16 / fp32: bias -> batch-norm inference -> ReLU (MIOpen's CBNA order).
-template <int DT>
-__device__ inline void epilogue_store_float(const float (&v)[16], const ConvArgs& a,
+template <int DT, int NCH = 16>
+__device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArgs& a,
                                             int m, int ch0, bool kvec) {
-  float t[16];
+  float t[NCH];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < NCH; ++e) {
     const int ch = ch0 + e;
     const bool live = kvec || ch < a.K;
     float x = v[e];
@@ -235,11 +247,11 @@ __device__ inline void epilogue_store_float(const float (&v)[16], const ConvArgs
     float* y = static_cast<float*>(a.y) + off;
     if (kvec) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NCH / 4; ++q)
         *reinterpret_cast<f32x4*>(y + 4 * q) = f32x4{t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < NCH; ++e)
         if (ch0 + e < a.K) y[e] = t[e];
     }
   } else {
@@ -249,13 +261,13 @@ __device__ inline void epilogue_store_float(const float (&v)[16], const ConvArgs
       i32x4 v[2];
     } o;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o.h[e] = f32_to_bf16_rne(t[e]);
+    for (int e = 0; e < NCH; ++e) o.h[e] = f32_to_bf16_rne(t[e]);
     if (kvec) {
-      reinterpret_cast<i32x4*>(y)[0] = o.v[0];
-      reinterpret_cast<i32x4*>(y)[1] = o.v[1];
+#pragma unroll
+      for (int q = 0; q < NCH / 8; ++q) reinterpret_cast<i32x4*>(y)[q] = o.v[q];
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < NCH; ++e)
         if (ch0 + e < a.K) y[e] = o.h[e];
     }
   }
@@ -575,44 +587,59 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint
 
 // LDS-tiled implicit GEMM for reductions too long to keep the filter slice
 // resident (bf16 / fp32 256-channel layers, int8 strided layers).  Workgroup
-// tile: 128 pixels x 128 output channels, 4 waves in a 2 x 2 grid of 64 x 64.
+// tile: 128 pixels x 128 output channels, 8 waves (two per SIMD, so one
+// wave's fragment reads, copies and barrier waits overlap the other's MFMAs)
+// in a 2 x 4 grid of 64 pixels x 32 channels.
 // The reduction advances in stages of 128 bytes (one filter tap, 128 bytes of
-// its channels; two MFMA k-steps).  Per stage every thread fetches 4 pixel-row
-// and 4 filter-row pieces of 16 bytes with buffer loads -- taps in the
-// padding and rows past M or Kp read zeros -- two stages ahead into a
-// register ring, and writes a fetched stage into one half of a double-buffered
-// LDS area.  LDS rows are 144 bytes (128 + 16 pad, an odd multiple of 16):
-// the 16 rows one ds_read_b128 touches fall in distinct bank groups.  Each
-// wave does a 4 x 4 grid of 16x16 MFMAs per k-step: 8 fragment reads feed 16
-// MFMAs.
-constexpr int kTileBM = 128, kTileBN = 128, kTileStage = 128, kTileRow = kTileStage + 16;
+// its channels; two MFMA k-steps).  A stage of the tile (128 pixel rows and
+// 128 filter rows of 128 bytes) arrives by buffer->LDS copies: 32 copies of
+// 1 KiB, 4 per wave, into one of three LDS stage buffers, two stages ahead of
+// the one being computed; taps in the padding and rows past M or Kp read
+// zeros.  Row r holds its 16-byte chunk c at slot c ^ (r & 7): a copy of 8
+// whole rows lands contiguously, and the 16 rows one fragment read touches
+// spread over all slots (contention-free ds_read_b128).  Each wave does a
+// 4 x 2 grid of 16x16 MFMAs per k-step: 6 fragment reads feed 8 MFMAs.  A
+// wave holds two of the four 16-row MFMA tiles of a 64-row packed filter
+// block, so each lane owns 8 consecutive output channels.
+constexpr int kTileBM = 128, kTileBN = 128, kTileStage = 128;
+constexpr int kTileBuf = (kTileBM + kTileBN) * kTileStage;  // 32 KiB
+
+constexpr int kTileThreads = 512;
 
 template <int DT, bool KVEC>
-__global__ __launch_bounds__(kThreads) void conv_tile_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void conv_tile_kernel(ConvArgs a) {
   using Acc = typename Dt<DT>::Acc;
   constexpr int E = Dt<DT>::kChunk;
   constexpr int ES = 16 / E;
   constexpr int SE = kTileStage / ES;  // reduction elements per stage
-  __shared__ __attribute__((aligned(16))) char lds[2][(kTileBM + kTileBN) * kTileRow];
+  // Three distinct arrays, so that reading one stage never waits for the
+  // copies still in flight into the others.
+  __shared__ __attribute__((aligned(1024))) char buf0[kTileBuf];
+  __shared__ __attribute__((aligned(1024))) char buf1[kTileBuf];
+  __shared__ __attribute__((aligned(1024))) char buf2[kTileBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // 64-pixel half, 32-channel quarter
   const int g = lane >> 4, col = lane & 15;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
 
-  // Loader role: rows r0 + 32h (h = 0..3) of both tiles, 16-byte piece q.
-  const int q = tid & 7;
-  const int r0 = tid >> 3;
-  int hb[4], wb[4], pbase[4];
-  uint32_t wbase[4];
+  // Copy role: copy h (h = 0, 1) of this wave covers pixel rows
+  // 64h + 8*wave .. +7 and copy 2+h the filter rows 128 + the same; lane l
+  // fills slot l & 7 of row 8*wave + 64h + (l >> 3), i.e. chunk
+  // q = (l & 7) ^ ((l >> 3) & 7) of that row.
+  const int r0 = 8 * wave + (lane >> 3);
+  const int q = (lane & 7) ^ ((lane >> 3) & 7);
+  int hb[2], wb[2], pbase[2];
+  uint32_t wbase[2];
   const int RS = a.wrow_bytes;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const int m = blockIdx.x * kTileBM + r0 + 32 * h;
+  for (int h = 0; h < 2; ++h) {
+    const int m = blockIdx.x * kTileBM + r0 + 64 * h;
     const int mm = m < a.M ? m : 0;
     const uint32_t qq = fast_div(static_cast<uint32_t>(mm), a.wo_mul, a.wo_add, a.wo_shift);
     const int wo = mm - static_cast<int>(qq) * a.Wo;
@@ -621,103 +648,133 @@ __global__ __launch_bounds__(kThreads) void conv_tile_kernel(ConvArgs a) {
     hb[h] = m < a.M ? ho * a.sh - a.pt : -(1 << 20);
     wb[h] = wo * a.sw - a.pl;
     pbase[h] = static_cast<int>(n) * a.H * a.W * a.C * ES + q * 16;
-    wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + r0 + 32 * h) * RS + q * 16);
+    wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + r0 + 64 * h) * RS + q * 16);
   }
 
-  const int cs = a.C / SE;  // stages per filter tap
-  const int nst = a.R * a.S * cs;
-  auto fetch = [&](int st, i32x4(&px)[4], i32x4(&fl)[4]) {
-    const int tap = st / cs;
-    const int c0b = (st - tap * cs) * kTileStage;
-    const int r = tap / a.S;
-    const int s = tap - r * a.S;
+  const int nst = a.R * a.S * (a.C / SE);
+  const int CB = a.C * ES;  // bytes of one tap's channels
+  // Position of the next stage to copy: channel byte offset c0b inside tap
+  // (r, s), advanced one stage per call (no divisions).
+  int nx_st = 0, nx_c0b = 0, nx_r = 0, nx_s = 0;
+  // This wave's 4 copies of the next stage (past the last stage: zeros).
+  auto issue = [&](char* buf) {
+    const int st = nx_st, c0b = nx_c0b, r = nx_r, s = nx_s;
+    ++nx_st;
+    nx_c0b += kTileStage;
+    if (nx_c0b == CB) {
+      nx_c0b = 0;
+      if (++nx_s == a.S) {
+        nx_s = 0;
+        ++nx_r;
+      }
+    }
     const bool live = st < nst;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < 2; ++h) {
       const int hi = hb[h] + r, wi = wb[h] + s;
       const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
                       static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
       const uint32_t off =
           ok ? static_cast<uint32_t>(pbase[h] + (hi * a.W + wi) * a.C * ES + c0b) : kOutOfRange;
-      px[h] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-      fl[h] = __builtin_amdgcn_raw_buffer_load_b128(
-          wr, live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_ptr_t)(buf + (8 * wave + 64 * h) * kTileStage), 16, off, 0, 0, 0);
     }
-  };
-  auto stash = [&](int buf, const i32x4(&px)[4], const i32x4(&fl)[4]) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      *reinterpret_cast<i32x4*>(&lds[buf][(r0 + 32 * h) * kTileRow + q * 16]) = px[h];
-      *reinterpret_cast<i32x4*>(&lds[buf][(kTileBM + r0 + 32 * h) * kTileRow + q * 16]) = fl[h];
-    }
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_ptr_t)(buf + (kTileBM + 8 * wave + 64 * h) * kTileStage), 16,
+          live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0, 0);
   };
 
-  Acc acc[4][4];
+  Acc acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-  auto compute = [&](int buf) {
+  // Fragment rows: pixel row wm*64 + 16i + col, filter row 128 + wn*32 +
+  // 16j + col; both have (row & 7) == (col & 7).
+  // Both k-steps' 12 fragments are read first, so the second k-step's reads
+  // complete under the first k-step's MFMAs.
+  auto compute = [&](const char* buf) {
+    i32x4 pf[2][4], ff[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const char* pl = &lds[buf][(wm * 64 + col) * kTileRow + kk * 64 + g * 16];
-      const char* fb = &lds[buf][(kTileBM + wn * 64 + col) * kTileRow + kk * 64 + g * 16];
-      i32x4 pf[4], ff[4];
+      const uint32_t slot = static_cast<uint32_t>(((kk * 4 + g) ^ (col & 7)) * 16);
+      const char* pl = buf + (wm * 64 + col) * kTileStage + slot;
+      const char* fb = buf + (kTileBM + wn * 32 + col) * kTileStage + slot;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileRow);
+      for (int i = 0; i < 4; ++i) pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ff[j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileRow);
+      for (int j = 0; j < 2; ++j) ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = mma_chunk(ff[j], pf[i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
-    }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mma_chunk(ff[kk][j], pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
+    // Issue every MFMA before the next stage's wait and barrier (otherwise
+    // the scheduler hoists the barrier above them and the MFMAs queue behind
+    // the barrier wait).
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Each wave waits for its own copies of the stage (the next stage's 4 may
+  // still be in flight) and for its own fragment reads, then a plain
+  // s_barrier: LDS has no cache, so every wave's copies are visible after
+  // it, and no wave still reads the previous stage's buffer, which the copies
+  // issued next reuse.  (__syncthreads() would add a release fence that
+  // waits for all copies.)
+  auto step = [&](const char* cur, char* next2) {
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(next2);  // stage + 2
+    compute(cur);
   };
 
-  // Two stages of loads in flight (registers A and B alternate), one stage
-  // being computed from LDS.
-  // Stages go in pairs with no exit in between (one back-edge keeps the
-  // accumulators in place); fetches past the last stage read zeros.
-  i32x4 pxA[4], flA[4], pxB[4], flB[4];
-  fetch(0, pxA, flA);
-  fetch(1, pxB, flB);
-  stash(0, pxA, flA);
-  __syncthreads();
-  for (int st = 0; st + 2 <= nst; st += 2) {
-    fetch(st + 2, pxA, flA);
-    compute(0);          // stage st
-    stash(1, pxB, flB);  // stage st+1
-    __syncthreads();
-    fetch(st + 3, pxB, flB);
-    compute(1);          // stage st+1
-    stash(0, pxA, flA);  // stage st+2
-    __syncthreads();
+  // Stage st lives in buffer st % 3.  Whole trips of three stages in the
+  // loop (no exit in between, so the accumulators stay in place), the rest
+  // after it.
+  issue(buf0);
+  issue(buf1);
+  int st = 0;
+  for (; st + 3 <= nst; st += 3) {
+    step(buf0, buf2);
+    step(buf1, buf0);
+    step(buf2, buf1);
   }
-  if (nst & 1) compute(0);  // the last stage, already in buffer 0
+  if (st < nst) step(buf0, buf2);
+  if (st + 1 < nst) step(buf1, buf0);
+  __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
-  const int ch0 = blockIdx.y * kTileBN + wn * 64 + 16 * g;
+  // Packed row blockIdx.y*128 + wn*32 + 16j + 4g + v is channel
+  // 64*(2*blockIdx.y + wn/2) + 16g + 8*(wn%2) + 4j + v: 8 consecutive
+  // channels per lane.
+  const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
   if (ch0 >= a.K) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
     if (m >= a.M) continue;
     if constexpr (DT == FCONV_INT8) {
-      int32_t v[16];
+      int32_t v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      const i32x4 sc = a.use_side ? load_side_chunk(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
-      epilogue_store_i8(v, a, m, ch0, KVEC, sc);
+      const i32x4 sc = a.use_side ? load_side_chunk<8>(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
+      epilogue_store_i8<8>(v, a, m, ch0, KVEC, sc);
     } else {
-      float v[16];
+      float v[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      epilogue_store_float<DT>(v, a, m, ch0, KVEC);
+      epilogue_store_float<DT, 8>(v, a, m, ch0, KVEC);
     }
   }
 }
@@ -1535,7 +1592,7 @@ template <int DT>
 hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p->M + kTileBM - 1) / kTileBM),
                   static_cast<unsigned>((p->Kp + kTileBN - 1) / kTileBN));
-  hipLaunchKernelGGL((conv_tile_kernel<DT, true>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((conv_tile_kernel<DT, true>), grid, dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
 }
 
