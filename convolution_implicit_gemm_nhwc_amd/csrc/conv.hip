@@ -1127,15 +1127,17 @@ void conv_stream_i8_kernel(ConvArgs a) {
 // Stride-1 int8 convolution over 64 input channels (one 64-byte k-step per
 // filter tap) for short reductions such as 3x3x64.  A workgroup owns
 // `halo_rows` consecutive output rows (flattened n*Ho + ho) and one 64-channel
-// slice of the filter, split into two phases of rows.  At start it issues
-// every load it will need as buffer->LDS copies: the filter slice, then for
-// each phase each distinct input row of the phase's footprint (zero rows and
-// zero columns for the padding come from out-of-range buffer offsets, which
-// read as zero) and the phase's side-input tile.  Phase A's data lands first;
-// its tiles are computed while phase B's copies are still in flight (each
-// phase stages into its own LDS arrays, so reading one does not wait for
-// copies into the other).  B fragments are read from LDS, so no tile waits on
-// device memory.
+// slice of the filter, split into two phases of rows: phase A is one row,
+// phase B the rest.  At start it issues every load it will need as
+// buffer->LDS copies: the filter slice, then for each phase each distinct
+// input row of the phase's footprint (zero rows and zero columns for the
+// padding come from out-of-range buffer offsets, which read as zero) and the
+// phase's side-input tile.  Copies issue at a limited rate per wave, so the
+// MFMA waves copy only the filter slice and phase A's rows and start
+// computing as soon as those land, while the epilogue waves copy the bias,
+// the side tiles and phase B's rows (each phase stages into its own LDS
+// arrays, so reading one does not wait for copies into another).  B
+// fragments are read from LDS, so no tile waits on device memory.
 //
 // Each input row lives in a 4 KiB slot: pixel X (halo column, X = input
 // column + left pad) holds its four 16-byte channel chunks at positions
@@ -1147,13 +1149,18 @@ void conv_stream_i8_kernel(ConvArgs a) {
 // rows of one image share R-1 input rows, and each image change skips R-1
 // slots so that rows of different images never collide.
 //
-// Four pixel waves walk every 4th 16-pixel tile of a phase; each is a pair
-// of waves that split the 64 channels (32 each, 8 outputs per lane), two
-// waves per SIMD, so one wave's requantisation VALU work runs while the
-// other's MFMAs occupy the matrix core.
+// Waves 0-3 (one per SIMD) are MFMA waves: each walks every 4th 16-pixel
+// tile of a phase with the whole 64-channel filter slice in registers and
+// hands its int32 accumulators through LDS to epilogue wave 4-7 on the same
+// SIMD, which requantises, adds the side input and stores.  The requantisation
+// costs about as much SIMD time as the contraction; a VALU-only wave next to an
+// MFMA-only wave overlaps the two, which a single wave doing both cannot.
+// Steps are separated by workgroup barriers; the hand-off is double-buffered.
 constexpr int kHaloSlot = 4096;
-constexpr int kHaloSlots = 7;       // input-row slots per phase
-constexpr int kHaloSidePx = 256;    // side-tile pixels per phase
+constexpr int kHaloSlotsA = 3;      // input-row slots of phase A (one output row)
+constexpr int kHaloSlotsB = 9;      // input-row slots of phase B
+constexpr int kHaloSideA = 64;      // side-tile pixels of phase A
+constexpr int kHaloSideB = 384;     // side-tile pixels of phase B
 constexpr int kHaloThreads = 512;
 
 __device__ inline uint32_t halo_pos(int x, int c) {
@@ -1183,34 +1190,16 @@ __device__ inline HaloPhase halo_phase(const ConvArgs& a, int p0, int p1, int R)
   return h;
 }
 
-// s_waitcnt with vmcnt = min(n, 15) (expcnt and lgkmcnt not waited on).
-// Waiting with a smaller count than needed is always safe.
-__device__ inline void wait_vmcnt_at_most(int n) {
-  switch (n < 15 ? n : 15) {
-#define FCONV_VMWAIT(k) \
-  case k:               \
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (k));  \
-    break;
-    FCONV_VMWAIT(0) FCONV_VMWAIT(1) FCONV_VMWAIT(2) FCONV_VMWAIT(3) FCONV_VMWAIT(4)
-    FCONV_VMWAIT(5) FCONV_VMWAIT(6) FCONV_VMWAIT(7) FCONV_VMWAIT(8) FCONV_VMWAIT(9)
-    FCONV_VMWAIT(10) FCONV_VMWAIT(11) FCONV_VMWAIT(12) FCONV_VMWAIT(13) FCONV_VMWAIT(14)
-    default:
-      __builtin_amdgcn_s_waitcnt(0x0f70 | 15);
-      break;
-#undef FCONV_VMWAIT
-  }
-}
-
 template <int R, int S, bool SIDE>
 __global__ __launch_bounds__(kHaloThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_halo_i8_kernel(ConvArgs a) {
   constexpr int NKS = R * S;
   constexpr int RSB = NKS * 64 + 16;  // packed filter row bytes
   __shared__ __attribute__((aligned(16))) char wlds[64 * RSB];
-  __shared__ __attribute__((aligned(256))) char xa[kHaloSlots * kHaloSlot];
-  __shared__ __attribute__((aligned(256))) char xb[kHaloSlots * kHaloSlot];
-  __shared__ __attribute__((aligned(256))) char sa[SIDE ? kHaloSidePx * 64 : 16];
-  __shared__ __attribute__((aligned(256))) char sb[SIDE ? kHaloSidePx * 64 : 16];
+  __shared__ __attribute__((aligned(256))) char xa[kHaloSlotsA * kHaloSlot];
+  __shared__ __attribute__((aligned(256))) char xb[kHaloSlotsB * kHaloSlot];
+  __shared__ __attribute__((aligned(256))) char sa[SIDE ? kHaloSideA * 64 : 16];
+  __shared__ __attribute__((aligned(256))) char sb[SIDE ? kHaloSideB * 64 : 16];
   // Accumulator hand-off, per MFMA wave and step parity: chunk q (accumulator
   // tile q, 4 int32) of lane l at q * 1024 + 16 * l.
   __shared__ __attribute__((aligned(256))) char accb[4 * 2 * 4096];
@@ -1232,9 +1221,9 @@ void conv_halo_i8_kernel(ConvArgs a) {
   const int g0 = b * a.halo_rows;
   if (g0 >= rows_total) return;  // uniform per workgroup
   const int g1 = min(g0 + a.halo_rows, rows_total);
-  const int gm = min(g0 + a.halo_rows_a, g1);
-  const HaloPhase PA = halo_phase(a, g0, gm, R);
-  const HaloPhase PB = halo_phase(a, gm, g1, R);
+  const int ga = min(g0 + a.halo_rows_a, g1);
+  const HaloPhase PA = halo_phase(a, g0, ga, R);
+  const HaloPhase PB = halo_phase(a, ga, g1, R);
   const int sA = (PA.ntile + 3) >> 2;  // steps of each phase (4 tiles per step)
   const int sB = (PB.ntile + 3) >> 2;
 
@@ -1283,40 +1272,20 @@ void conv_halo_i8_kernel(ConvArgs a) {
   };
 
   if (mfma_role) {
-    // MFMA waves copy, in this order: filter slice, phase A rows, phase B
-    // rows, phase B side tile; they then wait for all but their phase-B
-    // copies.  They issue no stores, so a later wait for the phase-B copies
-    // never waits for output writes.
-    const int n_filter = RSB / 16;  // 64 rows of RSB bytes = RSB/16 KiB
-    const int e1 = n_filter, e2 = e1 + 4 * PA.nslots, e3 = e2 + 4 * PB.nslots;
-    const int e4 = e3 + (SIDE ? PB.ntile : 0);
-    for (int i = m; i < e4; i += 4) {
+    // MFMA waves copy the filter slice and phase A's rows, then wait for
+    // them: the first step needs nothing else.
+    const int e1 = RSB / 16;  // 64 rows of RSB bytes = RSB/16 KiB
+    const int e2 = e1 + 4 * PA.nslots;
+    for (int i = m; i < e2; i += 4) {
       if (i < e1) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wr, (lds_ptr_t)(wlds + i * 1024), 16,
             static_cast<uint32_t>(blockIdx.y * 64 * RSB + i * 1024 + lane * 16), 0, 0, 0);
-      } else if (i < e2) {
+      } else {
         copy_rows(PA, xa, i - e1);
-      } else if (i < e3) {
-        copy_rows(PB, xb, i - e2);
-      } else {
-        copy_side(PB, sb, i - e3);
       }
     }
-    const int first_b = e2 + ((m - e2) % 4 + 4) % 4;  // first index >= e2 with i % 4 == m
-    wait_vmcnt_at_most(first_b < e4 ? (e4 - first_b + 3) / 4 : 0);
-  } else {
-    // Epilogue waves copy the bias and the phase A side tile.
-    const int e1 = 1, e2 = e1 + (SIDE ? PA.ntile : 0);
-    for (int i = m; i < e2; i += 4) {
-      if (i == 0) {
-        const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
-                                       : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
-      } else {
-        copy_side(PA, sa, i - e1);
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
   // Every wave has waited for the copies the next step reads before it
   // arrives, and LDS has no cache, so a plain s_barrier publishes them.
@@ -1327,7 +1296,29 @@ void conv_halo_i8_kernel(ConvArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  barrier();
+  barrier();  // the MFMA waves' copies (filter slice, phase A rows) have landed
+  if (!mfma_role) {
+    // Epilogue waves copy the bias, the phase A side tile, phase B's rows
+    // and side tile, after the first barrier so that the first step's data
+    // has the memory system to itself.  They wait for them before the
+    // barrier that ends step 0, before they store anything, and phase B is
+    // computed from step 1 on.
+    const int e1 = 1, e2 = e1 + (SIDE ? PA.ntile : 0);
+    const int e3 = e2 + 4 * PB.nslots, e4 = e3 + (SIDE ? PB.ntile : 0);
+    for (int i = m; i < e4; i += 4) {
+      if (i == 0) {
+        const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
+                                       : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
+      } else if (i < e2) {
+        copy_side(PA, sa, i - e1);
+      } else if (i < e3) {
+        copy_rows(PB, xb, i - e2);
+      } else {
+        copy_side(PB, sb, i - e3);
+      }
+    }
+  }
 
   if (mfma_role) {
     i32x4 Wf[NKS][4];
@@ -1341,7 +1332,7 @@ void conv_halo_i8_kernel(ConvArgs a) {
     // One phase of MFMA steps.  Step ls computes tile m + 4*ls (lanes past
     // the phase's pixels read the last pixel; their results are never
     // stored) and hands its accumulators to the epilogue wave of this SIMD.
-    auto mfma_phase = [&](const HaloPhase& P, const char* xbuf, int steps, int step0, bool last) {
+    auto mfma_phase = [&](const HaloPhase& P, const char* xbuf, int steps, int step0) {
       if (steps == 0) return;
       // LDS addresses of the tile of step ls for this lane: tap (r, s) is
       // ad[s] + r * kHaloSlot.
@@ -1389,18 +1380,19 @@ void conv_halo_i8_kernel(ConvArgs a) {
         char* dst = accb + (m * 2 + ((step0 + ls) & 1)) * 4096 + 16 * lane;
 #pragma unroll
         for (int j = 0; j < 4; ++j) *reinterpret_cast<i32x4*>(dst + j * 1024) = acc[j];
-        if (last && ls + 1 == steps) __builtin_amdgcn_s_waitcnt(0);  // this wave's phase-B copies
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
         barrier();
       }
     };
-    mfma_phase(PA, xa, sA, 0, true);
-    mfma_phase(PB, xb, sB, sA, false);
+    // Phase A always has a step (one row); phase B's data was published by
+    // the barrier that ends step 0.
+    mfma_phase(PA, xa, sA, 0);
+    mfma_phase(PB, xb, sB, sA);
     barrier();  // the epilogue waves' last step
   } else {
     // Step 0 (the MFMA waves compute the first tiles): wait for this wave's
-    // copies (bias, phase A side tile) before the barrier that publishes
-    // them to the other epilogue waves; no output has been stored yet, so
+    // copies (bias, side tiles, phase B's rows) before the barrier that
+    // publishes them to the other waves; no output has been stored yet, so
     // this waits for nothing else.
     __builtin_amdgcn_s_waitcnt(0);
     barrier();
@@ -1532,23 +1524,26 @@ hipError_t launch_stream(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-// Whether every phase of the row-halo kernel fits its LDS arrays when each
-// workgroup takes `rows` output rows (the first ceil(rows/2) in phase A):
-// input-row slots (rows + (R-1) per image the phase touches) and side
-// pixels, checked exactly for every workgroup.
+// Whether both phases of the row-halo kernel fit their LDS arrays when each
+// workgroup takes `rows` output rows (phase A one row, phase B the rest):
+// input-row slots (rows + (R-1) per image the phase touches) and side pixels,
+// checked exactly for every workgroup.
 bool halo_fits(const fconv_plan_s* p, int rows) {
   const int64_t rows_total = static_cast<int64_t>(p->d.N) * p->Ho;
-  const int ra = (rows + 1) / 2;
-  if (static_cast<int64_t>(ra) * p->Wo > kHaloSidePx) return false;
+  const int slots[2] = {kHaloSlotsA, kHaloSlotsB};
+  const int side[2] = {kHaloSideA, kHaloSideB};
+  const int len[2] = {1, rows - 1};
+  for (int ph = 0; ph < 2; ++ph)
+    if (static_cast<int64_t>(len[ph]) * p->Wo > side[ph]) return false;
   for (int64_t g0 = 0; g0 < rows_total; g0 += rows) {
-    const int64_t g1 = std::min<int64_t>(g0 + rows, rows_total);
-    const int64_t gm = std::min<int64_t>(g0 + ra, g1);
-    const int64_t bounds[3] = {g0, gm, g1};
+    int64_t p0 = g0;
     for (int ph = 0; ph < 2; ++ph) {
-      const int64_t p0 = bounds[ph], p1 = bounds[ph + 1];
-      if (p1 <= p0) continue;
-      const int64_t images = (p1 - 1) / p->Ho - p0 / p->Ho + 1;
-      if ((p1 - p0) + (p->d.R - 1) * images > kHaloSlots) return false;
+      const int64_t p1 = std::min<int64_t>(p0 + len[ph], rows_total);
+      if (p1 > p0) {
+        const int64_t images = (p1 - 1) / p->Ho - p0 / p->Ho + 1;
+        if ((p1 - p0) + (p->d.R - 1) * images > slots[ph]) return false;
+      }
+      p0 = std::max(p0, p1);
     }
   }
   return true;
@@ -1561,12 +1556,11 @@ hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStrea
   const int rows_total = p->d.N * p->Ho;
   int rows = p->halo_rows > 0 ? std::min(p->halo_rows, rows_total)
                               : (rows_total + cus - 1) / cus;
-  // Two phases of ceil(rows/2) and floor(rows/2) rows, each within one
-  // phase's LDS arrays.
+  // Two phases (one row, then the rest), each within its LDS arrays.
   while (rows > 1 && !halo_fits(p, rows)) --rows;
   if (!halo_fits(p, rows)) return hipErrorInvalidValue;
   a.halo_rows = rows;
-  a.halo_rows_a = (rows + 1) / 2;
+  a.halo_rows_a = 1;
   const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows), static_cast<unsigned>(p->Kp / 64));
   if (a.use_side)
     hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true>), g, dim3(kHaloThreads), 0, s, a);
