@@ -1127,24 +1127,27 @@ void conv_stream_i8_kernel(ConvArgs a) {
 // Stride-1 int8 convolution over 64 input channels (one 64-byte k-step per
 // filter tap) for short reductions such as 3x3x64.  A workgroup owns
 // `halo_rows` consecutive output rows (flattened n*Ho + ho) and one 64-channel
-// slice of the filter, split into two phases of rows: phase A is one row,
-// phase B the rest.  At start it issues every load it will need as
-// buffer->LDS copies: the filter slice, then for each phase each distinct
-// input row of the phase's footprint (zero rows and zero columns for the
-// padding come from out-of-range buffer offsets, which read as zero) and the
-// phase's side-input tile.  Copies issue at a limited rate per wave, so the
-// MFMA waves copy only the filter slice and phase A's rows and start
-// computing as soon as those land, while the epilogue waves copy the bias,
-// the side tiles and phase B's rows (each phase stages into its own LDS
-// arrays, so reading one does not wait for copies into another).  B
-// fragments are read from LDS, so no tile waits on device memory.
+// slice of the filter, split into two phases of rows: phase A is the first
+// two rows, phase B the rest.  Loads are buffer->LDS copies: the filter slice and, for
+// each phase, each distinct input row of the phase's footprint (zero rows and
+// zero columns for the padding come from out-of-range buffer offsets, which
+// read as zero).  Copies issue at a limited rate per CU, so the MFMA waves
+// copy only the filter slice and phase A's rows and start computing as soon
+// as those land, while the epilogue waves copy the bias and phase B's rows
+// (each phase stages into its own LDS array, so reading one does not wait
+// for copies into another).  B fragments are read from LDS, so no tile waits
+// on device memory.  The side input streams in during the steps instead:
+// each epilogue wave copies the 1 KiB side tile of its own tile two steps
+// ahead into a three-slot ring and waits for it with a fixed vmcnt (its
+// copies and stores alternate, and complete in issue order), so phase B's
+// rows are not queued behind side data.
 //
 // Each input row lives in a 4 KiB slot: pixel X (halo column, X = input
 // column + left pad) holds its four 16-byte channel chunks at positions
 // 4X + (c ^ ((X >> 1) & 3)); with that swizzle a wave reading 16 consecutive
 // pixels x one chunk per lane group runs at the contention-free ds_read_b128
-// rate for any starting pixel.  The side tile uses the same swizzle over the
-// phase's pixel index.  Slot of tap row r for phase row j of image n:
+// rate for any starting pixel.  A side tile uses the same swizzle over its
+// 16 pixels.  Slot of tap row r for phase row j of image n:
 // j + r + (R-1)*(n - n0), n0 = the phase's first image; consecutive output
 // rows of one image share R-1 input rows, and each image change skips R-1
 // slots so that rows of different images never collide.
@@ -1157,10 +1160,10 @@ void conv_stream_i8_kernel(ConvArgs a) {
 // MFMA-only wave overlaps the two, which a single wave doing both cannot.
 // Steps are separated by workgroup barriers; the hand-off is double-buffered.
 constexpr int kHaloSlot = 4096;
-constexpr int kHaloSlotsA = 3;      // input-row slots of phase A (one output row)
+constexpr int kHaloRowsA = 2;       // output rows of phase A
+constexpr int kHaloSlotsA = 6;      // input-row slots of phase A (two rows, up to two images)
 constexpr int kHaloSlotsB = 9;      // input-row slots of phase B
-constexpr int kHaloSideA = 64;      // side-tile pixels of phase A
-constexpr int kHaloSideB = 384;     // side-tile pixels of phase B
+constexpr int kHaloSideRing = 3;   // side-tile slots per epilogue wave
 constexpr int kHaloThreads = 512;
 
 __device__ inline uint32_t halo_pos(int x, int c) {
@@ -1198,8 +1201,7 @@ void conv_halo_i8_kernel(ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char wlds[64 * RSB];
   __shared__ __attribute__((aligned(256))) char xa[kHaloSlotsA * kHaloSlot];
   __shared__ __attribute__((aligned(256))) char xb[kHaloSlotsB * kHaloSlot];
-  __shared__ __attribute__((aligned(256))) char sa[SIDE ? kHaloSideA * 64 : 16];
-  __shared__ __attribute__((aligned(256))) char sb[SIDE ? kHaloSideB * 64 : 16];
+  __shared__ __attribute__((aligned(256))) char sring[SIDE ? 4 * kHaloSideRing * 1024 : 16];
   // Accumulator hand-off, per MFMA wave and step parity: chunk q (accumulator
   // tile q, 4 int32) of lane l at q * 1024 + 16 * l.
   __shared__ __attribute__((aligned(256))) char accb[4 * 2 * 4096];
@@ -1260,15 +1262,21 @@ void conv_halo_i8_kernel(ConvArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         xr, (lds_ptr_t)(xbuf + sigma * kHaloSlot + (k & 3) * 1024), 16, src, 0, 0, 0);
   };
-  auto copy_side = [&](const HaloPhase& P, char* sbuf, int k) {
-    const int pos = k * 64 + lane;
-    const int pp = pos >> 2;
-    const int c = (pos & 3) ^ ((pp >> 1) & 3);
+  // Side tile of this epilogue wave's tile at (global) step t into ring slot
+  // t % 3; past the last step it reads nothing (an out-of-range copy keeps
+  // the wave's count of memory operations per step fixed).
+  auto copy_side = [&](int t) {
+    const bool in_a = t < sA;
+    const int ls = in_a ? t : t - sA;
+    const int npx = in_a ? PA.npx : PB.npx;
+    const int pbase = (in_a ? PA.p0 : PB.p0) * a.Wo;
+    const int pp = (m + 4 * ls) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((pp >> 1) & 3);
     const int ch = blockIdx.y * 64 + 16 * c;
-    const bool ok = pp < P.npx && ch < a.K;
-    const uint32_t src =
-        ok ? static_cast<uint32_t>((P.p0 * a.Wo + pp) * a.K + ch) : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(sbuf + k * 1024), 16, src, 0, 0, 0);
+    const bool ok = t < sA + sB && pp < npx && ch < a.K;
+    const uint32_t src = ok ? static_cast<uint32_t>((pbase + pp) * a.K + ch) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        sr, (lds_ptr_t)(sring + (m * kHaloSideRing + t % kHaloSideRing) * 1024), 16, src, 0, 0, 0);
   };
 
   if (mfma_role) {
@@ -1298,24 +1306,23 @@ void conv_halo_i8_kernel(ConvArgs a) {
   };
   barrier();  // the MFMA waves' copies (filter slice, phase A rows) have landed
   if (!mfma_role) {
-    // Epilogue waves copy the bias, the phase A side tile, phase B's rows
-    // and side tile, after the first barrier so that the first step's data
-    // has the memory system to itself.  They wait for them before the
-    // barrier that ends step 0, before they store anything, and phase B is
-    // computed from step 1 on.
-    const int e1 = 1, e2 = e1 + (SIDE ? PA.ntile : 0);
-    const int e3 = e2 + 4 * PB.nslots, e4 = e3 + (SIDE ? PB.ntile : 0);
-    for (int i = m; i < e4; i += 4) {
+    // Epilogue waves copy the side tiles of their first two steps, the bias
+    // and phase B's rows, after the first barrier so that the first step's
+    // data has the memory system to itself.  They wait for them before the
+    // barrier that ends step 0, before they store anything; phase B is
+    // computed after that barrier.
+    if constexpr (SIDE) {
+      copy_side(0);
+      copy_side(1);
+    }
+    const int e3 = 1 + 4 * PB.nslots;
+    for (int i = m; i < e3; i += 4) {
       if (i == 0) {
         const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
                                        : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
-      } else if (i < e2) {
-        copy_side(PA, sa, i - e1);
-      } else if (i < e3) {
-        copy_rows(PB, xb, i - e2);
       } else {
-        copy_side(PB, sb, i - e3);
+        copy_rows(PB, xb, i - 1);
       }
     }
   }
@@ -1384,14 +1391,14 @@ void conv_halo_i8_kernel(ConvArgs a) {
         barrier();
       }
     };
-    // Phase A always has a step (one row); phase B's data was published by
-    // the barrier that ends step 0.
+    // Phase A always has a step; phase B's rows were published by the
+    // barrier that ends step 0, before phase B's first fragments are read.
     mfma_phase(PA, xa, sA, 0);
     mfma_phase(PB, xb, sB, sA);
     barrier();  // the epilogue waves' last step
   } else {
     // Step 0 (the MFMA waves compute the first tiles): wait for this wave's
-    // copies (bias, side tiles, phase B's rows) before the barrier that
+    // copies (side tiles, bias, phase B's rows) before the barrier that
     // publishes them to the other waves; no output has been stored yet, so
     // this waits for nothing else.
     __builtin_amdgcn_s_waitcnt(0);
@@ -1401,24 +1408,48 @@ void conv_halo_i8_kernel(ConvArgs a) {
     for (int e = 0; e < 16; ++e) bias[e] = blds[16 * g + e];
     const float cis = a.cis, sis = a.sis;
     const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
-    auto epi_phase = [&](const HaloPhase& P, const char* sbuf, int steps, int step0) {
+    auto epi_phase = [&](const HaloPhase& P, int steps, int step0) {
       for (int ls = 0; ls < steps; ++ls) {
-        const char* src = accb + (m * 2 + ((step0 + ls) & 1)) * 4096 + 16 * lane;
+        const int t = step0 + ls;
+        const char* src = accb + (m * 2 + (t & 1)) * 4096 + 16 * lane;
         i32x4 acc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = *reinterpret_cast<const i32x4*>(src + j * 1024);
         const int p = (m + 4 * ls) * 16 + col;
         i32x4 sd = i32x4{0, 0, 0, 0};
-        if constexpr (SIDE)
-          sd = *reinterpret_cast<const i32x4*>(sbuf + 16u * halo_pos(min(p, P.npx - 1), g));
+        if constexpr (SIDE) {
+          // The side tile of step t >= 2 was copied at step t - 2, after
+          // that step's store; the store of step t - 1 and the copy of step
+          // t + 1 have been issued since, so vmcnt(2) covers it (earlier
+          // tiles landed before the first step).  The reads are issued in
+          // one block with that wait: a compiler-generated read of the ring
+          // would wait for every copy in flight into it.
+          const char* sp = sring + (m * kHaloSideRing + t % kHaloSideRing) * 1024 +
+                           16u * halo_pos(col, g);
+          const uint32_t acc_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)src));
+          const uint32_t side_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)sp));
+          asm volatile(
+              "s_waitcnt vmcnt(2)\n\t"
+              "ds_read_b128 %0, %5\n\t"
+              "ds_read_b128 %1, %5 offset:1024\n\t"
+              "ds_read_b128 %2, %5 offset:2048\n\t"
+              "ds_read_b128 %3, %5 offset:3072\n\t"
+              "ds_read_b128 %4, %6\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(acc[0]), "=&v"(acc[1]), "=&v"(acc[2]), "=&v"(acc[3]), "=&v"(sd)
+              : "v"(acc_addr), "v"(side_addr)
+              : "memory");
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = *reinterpret_cast<const i32x4*>(src + j * 1024);
+        }
         const bool ok = p < P.npx && ch0 < a.K;
         const uint32_t off = ok ? static_cast<uint32_t>((P.p0 * a.Wo + p) * a.K + ch0) : kOutOfRange;
         stream_epilogue_i8<SIDE, 16>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
+        if constexpr (SIDE) copy_side(t + 2);  // into the slot step t - 1 read
         barrier();
       }
     };
-    epi_phase(PA, sa, sA, 0);
-    epi_phase(PB, sb, sB, sA);
+    epi_phase(PA, sA, 0);
+    epi_phase(PB, sB, sA);
   }
 }
 
@@ -1525,16 +1556,13 @@ hipError_t launch_stream(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s
 }
 
 // Whether both phases of the row-halo kernel fit their LDS arrays when each
-// workgroup takes `rows` output rows (phase A one row, phase B the rest):
-// input-row slots (rows + (R-1) per image the phase touches) and side pixels,
-// checked exactly for every workgroup.
+// workgroup takes `rows` output rows (phase A two rows, phase B the rest):
+// input-row slots (rows + (R-1) per image the phase touches), checked exactly
+// for every workgroup.
 bool halo_fits(const fconv_plan_s* p, int rows) {
   const int64_t rows_total = static_cast<int64_t>(p->d.N) * p->Ho;
   const int slots[2] = {kHaloSlotsA, kHaloSlotsB};
-  const int side[2] = {kHaloSideA, kHaloSideB};
-  const int len[2] = {1, rows - 1};
-  for (int ph = 0; ph < 2; ++ph)
-    if (static_cast<int64_t>(len[ph]) * p->Wo > side[ph]) return false;
+  const int len[2] = {std::min(kHaloRowsA, rows), rows - std::min(kHaloRowsA, rows)};
   for (int64_t g0 = 0; g0 < rows_total; g0 += rows) {
     int64_t p0 = g0;
     for (int ph = 0; ph < 2; ++ph) {
@@ -1556,11 +1584,10 @@ hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStrea
   const int rows_total = p->d.N * p->Ho;
   int rows = p->halo_rows > 0 ? std::min(p->halo_rows, rows_total)
                               : (rows_total + cus - 1) / cus;
-  // Two phases (one row, then the rest), each within its LDS arrays.
   while (rows > 1 && !halo_fits(p, rows)) --rows;
   if (!halo_fits(p, rows)) return hipErrorInvalidValue;
   a.halo_rows = rows;
-  a.halo_rows_a = 1;
+  a.halo_rows_a = std::min(kHaloRowsA, rows);
   const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows), static_cast<unsigned>(p->Kp / 64));
   if (a.use_side)
     hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true>), g, dim3(kHaloThreads), 0, s, a);
