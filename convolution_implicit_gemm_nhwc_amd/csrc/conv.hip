@@ -189,9 +189,22 @@ __device__ inline i32x4 load_side_chunk(const ConvArgs& a, int m, int ch0, bool 
 // int8: TensorFlow conv_ops_fused_int8.cc, BiasActivationOutputKernel (cuDNN 8
 // order).  v[e] is the int32 accumulator of channel ch0 + e; side_chunk holds
 // the int8 side input of the same NCH channels (ignored unless a.use_side).
+// The bias of a lane's NCH channels (0 past K), loaded once per lane: loads
+// issued after an output store would wait for it, as the compiler cannot rule
+// out that they alias.
+template <int NCH>
+__device__ inline void load_bias(const ConvArgs& a, int ch0, bool kvec, float (&bias)[NCH]) {
+#pragma unroll
+  for (int e = 0; e < NCH; ++e) {
+    const int ch = ch0 + e;
+    bias[e] = (kvec || ch < a.K) ? a.bias[ch] : 0.0f;
+  }
+}
+
 template <int NCH = 16>
 __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs& a,
-                                         int m, int ch0, bool kvec, i32x4 side_chunk) {
+                                         int m, int ch0, bool kvec, i32x4 side_chunk,
+                                         const float (&bias)[NCH]) {
   int8_t* y = static_cast<int8_t*>(a.y) + static_cast<int64_t>(m) * a.K + ch0;
   union {
     int8_t b[16];
@@ -202,8 +215,7 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
   const float lo = a.relu ? 0.0f : -128.0f;
 #pragma unroll
   for (int e = 0; e < NCH; ++e) {
-    const int ch = ch0 + e;
-    const float b = (kvec || ch < a.K) ? a.bias[ch] : 0.0f;
+    const float b = bias[e];
     float t = static_cast<float>(v[e]);        // int32 -> fp32, nearest even
     t = t * a.cis;                             // (1) scale
     if (a.use_side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);  // (2)
@@ -224,21 +236,45 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
   }
 }
 
+template <int NCH = 16>
+__device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs& a,
+                                         int m, int ch0, bool kvec, i32x4 side_chunk) {
+  float bias[NCH];
+  load_bias<NCH>(a, ch0, kvec, bias);
+  epilogue_store_i8<NCH>(v, a, m, ch0, kvec, side_chunk, bias);
+}
+
 // bf16 / fp32: bias -> batch-norm inference -> ReLU (MIOpen's CBNA order).
-template <int DT, int NCH = 16>
+// Per-channel values of the float epilogue for a lane's NCH channels, loaded
+// (and the batch-norm scale computed) once per lane; zero for channels past
+// K, whose outputs are never stored.
+template <int NCH>
+struct FloatEpiParams {
+  float bias[NCH], mean[NCH], sc[NCH], beta[NCH];
+  __device__ inline void load(const ConvArgs& a, int ch0, bool kvec) {
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) {
+      const int ch = ch0 + e;
+      const bool live = kvec || ch < a.K;
+      bias[e] = a.use_bias && live ? a.bias[ch] : 0.0f;
+      const bool bn = a.use_bn && live;
+      sc[e] = bn ? a.bn_gamma[ch] / __builtin_sqrtf(a.bn_var[ch] + a.bn_eps) : 0.0f;
+      mean[e] = bn ? a.bn_mean[ch] : 0.0f;
+      beta[e] = bn ? a.bn_beta[ch] : 0.0f;
+    }
+  }
+};
+
+template <int DT, int NCH>
 __device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArgs& a,
-                                            int m, int ch0, bool kvec) {
+                                            int m, int ch0, bool kvec,
+                                            const FloatEpiParams<NCH>& P) {
   float t[NCH];
 #pragma unroll
   for (int e = 0; e < NCH; ++e) {
-    const int ch = ch0 + e;
-    const bool live = kvec || ch < a.K;
     float x = v[e];
-    if (a.use_bias && live) x = x + a.bias[ch];
-    if (a.use_bn && live) {
-      const float sc = a.bn_gamma[ch] / __builtin_sqrtf(a.bn_var[ch] + a.bn_eps);
-      x = (x - a.bn_mean[ch]) * sc + a.bn_beta[ch];
-    }
+    if (a.use_bias) x = x + P.bias[e];
+    if (a.use_bn) x = (x - P.mean[e]) * P.sc[e] + P.beta[e];
     if (a.relu) x = __builtin_fmaxf(x, 0.0f);
     t[e] = x;
   }
@@ -271,6 +307,14 @@ __device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArg
         if (ch0 + e < a.K) y[e] = o.h[e];
     }
   }
+}
+
+template <int DT, int NCH = 16>
+__device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArgs& a,
+                                            int m, int ch0, bool kvec) {
+  FloatEpiParams<NCH> P;
+  P.load(a, ch0, kvec);
+  epilogue_store_float<DT, NCH>(v, a, m, ch0, kvec, P);
 }
 
 // ------------------------------------------------------------ general conv
@@ -593,8 +637,9 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint
 // The reduction advances in stages of 128 bytes (one filter tap, 128 bytes of
 // its channels; two MFMA k-steps).  A stage of the tile (128 pixel rows and
 // 128 filter rows of 128 bytes) arrives by buffer->LDS copies: 32 copies of
-// 1 KiB, 4 per wave, into one of three LDS stage buffers, two stages ahead of
-// the one being computed; taps in the padding and rows past M or Kp read
+// 1 KiB, 4 per wave, into one of four LDS stage buffers, three stages ahead
+// of the one being computed (the copies' latency under load is about three
+// stages' compute); taps in the padding and rows past M or Kp read
 // zeros.  Row r holds its 16-byte chunk c at slot c ^ (r & 7): a copy of 8
 // whole rows lands contiguously, and the 16 rows one fragment read touches
 // spread over all slots (contention-free ds_read_b128).  Each wave does a
@@ -613,11 +658,12 @@ void conv_tile_kernel(ConvArgs a) {
   constexpr int E = Dt<DT>::kChunk;
   constexpr int ES = 16 / E;
   constexpr int SE = kTileStage / ES;  // reduction elements per stage
-  // Three distinct arrays, so that reading one stage never waits for the
+  // Four distinct arrays, so that reading one stage never waits for the
   // copies still in flight into the others.
   __shared__ __attribute__((aligned(1024))) char buf0[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf1[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf2[kTileBuf];
+  __shared__ __attribute__((aligned(1024))) char buf3[kTileBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -649,6 +695,33 @@ void conv_tile_kernel(ConvArgs a) {
     wb[h] = wo * a.sw - a.pl;
     pbase[h] = static_cast<int>(n) * a.H * a.W * a.C * ES + q * 16;
     wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + r0 + 64 * h) * RS + q * 16);
+  }
+
+  // Packed row blockIdx.y*128 + wn*32 + 16j + 4g + v is channel
+  // 64*(2*blockIdx.y + wn/2) + 16g + 8*(wn%2) + 4j + v: 8 consecutive
+  // channels per lane.  The epilogue's loads (per-channel values, the four
+  // side chunks) are issued here, before the first copy, so that they land
+  // during the main loop (and no later than the first stage's copies).
+  const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
+  const bool ch_live = ch0 < a.K;
+  float bias_pre[8];
+  i32x4 side_pre[4];
+  FloatEpiParams<8> fpar;
+  if constexpr (DT == FCONV_INT8) {
+    if (ch_live) {
+      load_bias<8>(a, ch0, KVEC, bias_pre);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bias_pre[e] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+      side_pre[i] = a.use_side && ch_live && m < a.M ? load_side_chunk<8>(a, m, ch0, KVEC)
+                                                     : i32x4{0, 0, 0, 0};
+    }
+  } else {
+    fpar.load(a, ch_live ? ch0 : a.K, KVEC && ch_live);  // nothing loaded past K
   }
 
   const int nst = a.R * a.S * (a.C / SE);
@@ -694,87 +767,105 @@ void conv_tile_kernel(ConvArgs a) {
 
   // Fragment rows: pixel row wm*64 + 16i + col, filter row 128 + wn*32 +
   // 16j + col; both have (row & 7) == (col & 7).
-  // Both k-steps' 12 fragments are read first, so the second k-step's reads
-  // complete under the first k-step's MFMAs.
-  auto compute = [&](const char* buf) {
+  struct Frags {
     i32x4 pf[2][4], ff[2][2];
+  };
+  auto read_frags = [&](const char* buf, Frags& f) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint32_t slot = static_cast<uint32_t>(((kk * 4 + g) ^ (col & 7)) * 16);
       const char* pl = buf + (wm * 64 + col) * kTileStage + slot;
       const char* fb = buf + (kTileBM + wn * 32 + col) * kTileStage + slot;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
+      for (int i = 0; i < 4; ++i) f.pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
+      for (int j = 0; j < 2; ++j) f.ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = mma_chunk(ff[kk][j], pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
-    // Issue every MFMA before the next stage's wait and barrier (otherwise
+          acc[i][j] = mma_chunk(f.ff[kk][j], f.pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Step st computes stage st from fragments read during step st - 1 and
+  // reads stage st + 1's fragments while its MFMAs run, so the matrix core
+  // never waits for a stage's LDS reads.  Each wave first waits for its own
+  // copies of stage st + 1 (stage st + 2's 4 may still be in flight), then a
+  // plain s_barrier: LDS has no cache, so every wave's copies of stage st + 1
+  // are visible after it, and every wave has consumed stage st - 1, whose
+  // buffer the copies of stage st + 3 issued next reuse.  (__syncthreads()
+  // would add a release fence that waits for all copies.)
+  auto step = [&](const char* next, char* next3, const Frags& cur, Frags& nxt) {
+    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    barrier();
+    issue(next3);  // stage + 3, into the buffer of the stage before this one
+    read_frags(next, nxt);
+    // The reads go out before the MFMAs (left alone, the scheduler sinks
+    // them to the end of the step, and the next step's MFMAs wait on them).
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur);
+    // Issue every MFMA before the next step's wait and barrier (otherwise
     // the scheduler hoists the barrier above them and the MFMAs queue behind
     // the barrier wait).
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Each wave waits for its own copies of the stage (the next stage's 4 may
-  // still be in flight) and for its own fragment reads, then a plain
-  // s_barrier: LDS has no cache, so every wave's copies are visible after
-  // it, and no wave still reads the previous stage's buffer, which the copies
-  // issued next reuse.  (__syncthreads() would add a release fence that
-  // waits for all copies.)
-  auto step = [&](const char* cur, char* next2) {
-    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(next2);  // stage + 2
-    compute(cur);
-  };
 
-  // Stage st lives in buffer st % 3.  Whole trips of three stages in the
+  // Stage st lives in buffer st % 4.  Whole trips of four stages in the
   // loop (no exit in between, so the accumulators stay in place), the rest
-  // after it.
+  // after it.  Past the last stage the copies are zeros and the fragment
+  // reads unused.
   issue(buf0);
   issue(buf1);
+  issue(buf2);
+  Frags fa, fb;
+  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): this wave's copies of stage 0
+  barrier();
+  read_frags(buf0, fa);
   int st = 0;
-  for (; st + 3 <= nst; st += 3) {
-    step(buf0, buf2);
-    step(buf1, buf0);
-    step(buf2, buf1);
+  for (; st + 4 <= nst; st += 4) {
+    step(buf1, buf3, fa, fb);
+    step(buf2, buf0, fb, fa);
+    step(buf3, buf1, fa, fb);
+    step(buf0, buf2, fb, fa);
   }
-  if (st < nst) step(buf0, buf2);
-  if (st + 1 < nst) step(buf1, buf0);
+  if (st < nst) step(buf1, buf3, fa, fb);
+  if (st + 1 < nst) step(buf2, buf0, fb, fa);
+  if (st + 2 < nst) step(buf3, buf1, fa, fb);
   __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
-  // Packed row blockIdx.y*128 + wn*32 + 16j + 4g + v is channel
-  // 64*(2*blockIdx.y + wn/2) + 16g + 8*(wn%2) + 4j + v: 8 consecutive
-  // channels per lane.
-  const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
   if (ch0 >= a.K) return;
+  if constexpr (DT == FCONV_INT8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
-    if (m >= a.M) continue;
-    if constexpr (DT == FCONV_INT8) {
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+      if (m >= a.M) continue;
       int32_t v[8];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      const i32x4 sc = a.use_side ? load_side_chunk<8>(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
-      epilogue_store_i8<8>(v, a, m, ch0, KVEC, sc);
-    } else {
+      epilogue_store_i8<8>(v, a, m, ch0, KVEC, side_pre[i], bias_pre);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+      if (m >= a.M) continue;
       float v[8];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      epilogue_store_float<DT, 8>(v, a, m, ch0, KVEC);
+      epilogue_store_float<DT, 8>(v, a, m, ch0, KVEC, fpar);
     }
   }
 }
