@@ -809,10 +809,17 @@ void conv_tile_kernel(ConvArgs a) {
     barrier();
     issue(next3);  // stage + 3, into the buffer of the stage before this one
     read_frags(next, nxt);
-    // The reads go out before the MFMAs (left alone, the scheduler sinks
-    // them to the end of the step, and the next step's MFMAs wait on them).
-    __builtin_amdgcn_sched_barrier(0);
     mma(cur);
+    // Order: the fragment reads first (left alone, the scheduler sinks them
+    // to the end of the step, and the next step's MFMAs wait on them), then
+    // the copies spread between the MFMAs, so that a copy stalled on a busy
+    // memory pipe does not hold the matrix core idle.
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
+    }
     // Issue every MFMA before the next step's wait and barrier (otherwise
     // the scheduler hoists the barrier above them and the MFMAs queue behind
     // the barrier wait).
