@@ -1291,6 +1291,24 @@ __device__ inline HaloPhase halo_phase(const ConvArgs& a, int p0, int p1, int R)
   return h;
 }
 
+// s_waitcnt vmcnt(min(n, 15)) (expcnt and lgkmcnt not waited on); waiting
+// for fewer outstanding operations than allowed is always safe.
+__device__ inline void wait_vmcnt_at_most(int n) {
+  switch (n < 15 ? n : 15) {
+#define FCONV_VMWAIT(k)                         \
+  case k:                                       \
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (k));   \
+    break;
+    FCONV_VMWAIT(0) FCONV_VMWAIT(1) FCONV_VMWAIT(2) FCONV_VMWAIT(3) FCONV_VMWAIT(4)
+    FCONV_VMWAIT(5) FCONV_VMWAIT(6) FCONV_VMWAIT(7) FCONV_VMWAIT(8) FCONV_VMWAIT(9)
+    FCONV_VMWAIT(10) FCONV_VMWAIT(11) FCONV_VMWAIT(12) FCONV_VMWAIT(13) FCONV_VMWAIT(14)
+    default:
+      __builtin_amdgcn_s_waitcnt(0x0f70 | 15);
+      break;
+#undef FCONV_VMWAIT
+  }
+}
+
 template <int R, int S, bool SIDE>
 __global__ __launch_bounds__(kHaloThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_halo_i8_kernel(ConvArgs a) {
@@ -1377,12 +1395,12 @@ void conv_halo_i8_kernel(ConvArgs a) {
         sr, (lds_ptr_t)(sring + (m * kHaloSideRing + t % kHaloSideRing) * 1024), 16, src, 0, 0, 0);
   };
 
-  if (mfma_role) {
-    // MFMA waves copy the filter slice and phase A's rows, then wait for
-    // them: the first step needs nothing else.
+  {
+    // All eight waves copy the filter slice and phase A's rows, then wait
+    // for their own copies: the first step needs nothing else.
     const int e1 = RSB / 16;  // 64 rows of RSB bytes = RSB/16 KiB
     const int e2 = e1 + 4 * PA.nslots;
-    for (int i = m; i < e2; i += 4) {
+    for (int i = wave; i < e2; i += 8) {
       if (i < e1) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wr, (lds_ptr_t)(wlds + i * 1024), 16,
@@ -1402,13 +1420,13 @@ void conv_halo_i8_kernel(ConvArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  barrier();  // the MFMA waves' copies (filter slice, phase A rows) have landed
+  barrier();  // the filter slice and phase A's rows have landed
   if (!mfma_role) {
     // Epilogue waves copy the side tiles of their first two steps, the bias
     // and phase B's rows, after the first barrier so that the first step's
-    // data has the memory system to itself.  They wait for them before the
-    // barrier that ends step 0, before they store anything; phase B is
-    // computed after that barrier.
+    // data has the memory system to itself.  They wait for the side tiles
+    // and the bias before the barrier that ends step 0, and for phase B's
+    // rows before the barrier that ends the last phase-A step.
     if constexpr (SIDE) {
       copy_side(0);
       copy_side(1);
@@ -1496,10 +1514,18 @@ void conv_halo_i8_kernel(ConvArgs a) {
     barrier();  // the epilogue waves' last step
   } else {
     // Step 0 (the MFMA waves compute the first tiles): wait for this wave's
-    // copies (side tiles, bias, phase B's rows) before the barrier that
-    // publishes them to the other waves; no output has been stored yet, so
-    // this waits for nothing else.
-    __builtin_amdgcn_s_waitcnt(0);
+    // copies before the barrier that publishes them to the other waves; no
+    // output has been stored yet.  Phase B's first fragments are read after
+    // the barrier that ends the last phase-A step, so with two phase-A steps
+    // this wave's row copies (issued last) may stay in flight one step
+    // longer: they are waited for at the end of epilogue step 0, where the
+    // step's store and (with a side input) the copy of side tile 2 have been
+    // issued since.
+    const int rows_m = ((1 + 4 * PB.nslots - m + 3) >> 2) - ((1 - m + 3) >> 2);
+    if (sA >= 2)
+      wait_vmcnt_at_most(rows_m);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     barrier();
     float bias[16];
 #pragma unroll
@@ -1543,6 +1569,7 @@ void conv_halo_i8_kernel(ConvArgs a) {
         const uint32_t off = ok ? static_cast<uint32_t>((P.p0 * a.Wo + p) * a.K + ch0) : kOutOfRange;
         stream_epilogue_i8<SIDE, 16>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
         if constexpr (SIDE) copy_side(t + 2);  // into the slot step t - 1 read
+        if (t == 0 && sA >= 2) __builtin_amdgcn_s_waitcnt(SIDE ? 0x0f72 : 0x0f71);  // phase B's rows
         barrier();
       }
     };
