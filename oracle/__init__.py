@@ -62,6 +62,9 @@ def _load():
         lib.oracle_epilogue_i8.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p,
                                            ctypes.c_float, p, i, p]
         lib.oracle_epilogue_i8.restype = None
+        lib.oracle_epilogue_i8_ex.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p, p,
+                                              ctypes.c_float, p, i, i, p]
+        lib.oracle_epilogue_i8_ex.restype = None
         lib.oracle_epilogue_float.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
                                               ctypes.c_float, i, p]
         lib.oracle_epilogue_float.restype = None
@@ -146,8 +149,15 @@ def conv_acc(x, w, stride=1, padding="SAME", form="direct"):
 
 
 def epilogue_i8(acc, conv_input_scale, bias, side=None, side_input_scale=0.0,
-                relu=False):
-    """int8 fused epilogue over an NHWC int32 accumulator; returns int8 NHWC."""
+                relu=False, order=8):
+    """int8 fused epilogue over an NHWC int32 accumulator; returns int8 NHWC.
+
+    conv_input_scale: a scalar, or one fp32 value per output channel.
+    order: 8 (cuDNN 8 order: scale, side, bias) or 7 (cuDNN 7 order:
+    fmaf(acc, scale, bias), then side).
+    """
+    if order not in (7, 8):
+        raise OracleError("order must be 7 or 8")
     acc = np.ascontiguousarray(acc, dtype=np.int32)
     K = acc.shape[-1]
     M = acc.size // K
@@ -156,10 +166,16 @@ def epilogue_i8(acc, conv_input_scale, bias, side=None, side_input_scale=0.0,
         side = np.ascontiguousarray(side, dtype=np.int8)
         if side.shape != acc.shape:
             raise OracleError("side input must have the output's shape")
+    scales = None
+    if np.ndim(conv_input_scale) > 0:
+        scales = np.ascontiguousarray(conv_input_scale, dtype=np.float32).reshape(-1)
+        if scales.size != K:
+            raise OracleError("a conv_input_scale vector needs one value per output channel")
+        conv_input_scale = 0.0
     y = np.empty(acc.shape, dtype=np.int8)
-    _load().oracle_epilogue_i8(_ptr(acc), M, K, float(conv_input_scale), _ptr(side),
-                               float(side_input_scale), _ptr(bias), int(bool(relu)),
-                               _ptr(y))
+    _load().oracle_epilogue_i8_ex(_ptr(acc), M, K, float(conv_input_scale), _ptr(scales),
+                                  _ptr(side), float(side_input_scale), _ptr(bias),
+                                  int(bool(relu)), int(order), _ptr(y))
     return y
 
 
@@ -186,9 +202,9 @@ def epilogue_float(acc, bias=None, bn=None, relu=False):
 
 
 def fused_conv_i8(x, w, bias, conv_input_scale, side=None, side_input_scale=0.0,
-                  relu=False, stride=1, padding="SAME", form="direct"):
+                  relu=False, stride=1, padding="SAME", form="direct", order=8):
     acc = conv_acc(x, w, stride, padding, form)
-    return epilogue_i8(acc, conv_input_scale, bias, side, side_input_scale, relu)
+    return epilogue_i8(acc, conv_input_scale, bias, side, side_input_scale, relu, order)
 
 
 def fused_conv_float(x, w, bias=None, bn=None, relu=False, stride=1,

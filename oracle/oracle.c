@@ -42,6 +42,14 @@
  *    side_input_scale, t), one rounding, (3) t = t + bias[k]; then round half
  *    to even, clip to [-128, 127] (lower bound 0 under ReLU), cast to int8.
  *    All in fp32; the accumulator is converted to fp32 first.
+ *    Two variants from the same kernel: conv_input_scale may be a vector with
+ *    one value per output channel (the scale tensor of more than one element,
+ *    sliced at the output channel), and the cuDNN 7 order that the comment
+ *    there names, whose first step is one fused multiply-add
+ *    t = fmaf(acc, conv_input_scale, bias) and whose second is the same side
+ *    step as above (read as fmaf(side, side_input_scale, t): the comment
+ *    writes both orders' side step alike, and the cuDNN 8 code spells it that
+ *    way), with no separate bias step.
  *
  *  - The float epilogue.  MIOpen "Using the fusion API": operators apply in
  *    the order they are added, and the supported-fusion tables list
@@ -306,9 +314,15 @@ int oracle_conv_bf16_direct(const uint16_t* x, const uint16_t* w, const int* d,
  * TensorFlow output kernel spells it.  side may be NULL (no side input).
  * Every step is a separate fp32 operation; only step (2) is fused.
  */
-void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scale,
-                        const int8_t* side, float side_input_scale,
-                        const float* bias, int relu, int8_t* y) {
+/*
+ * int8 epilogue.  scales == NULL: every channel uses conv_input_scale;
+ * otherwise channel k uses scales[k].  order 8: cuDNN 8 order; order 7:
+ * cuDNN 7 order (see the header).
+ */
+void oracle_epilogue_i8_ex(const int32_t* acc, long M, int K, float conv_input_scale,
+                           const float* scales, const int8_t* side,
+                           float side_input_scale, const float* bias, int relu,
+                           int order, int8_t* y) {
   const float hi = 127.0f;
   const float lo = relu ? 0.0f : -128.0f;
   const int use_side = side != NULL && side_input_scale != 0.0f;
@@ -316,17 +330,30 @@ void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scal
   for (long m = 0; m < M; ++m) {
     for (int k = 0; k < K; ++k) {
       long i = m * K + k;
+      const float cis = scales ? scales[k] : conv_input_scale;
       float t = (float)acc[i];          /* int32 -> fp32, round to nearest even */
-      t = t * conv_input_scale;          /* (1) scale */
-      if (use_side)                      /* (2) side input, single rounding */
-        t = fmaf((float)side[i], side_input_scale, t);
-      t = t + bias[k];                   /* (3) bias */
+      if (order == 7) {
+        t = fmaf(t, cis, bias[k]);       /* scale and bias, single rounding */
+        if (use_side) t = fmaf((float)side[i], side_input_scale, t);
+      } else {
+        t = t * cis;                     /* (1) scale */
+        if (use_side)                    /* (2) side input, single rounding */
+          t = fmaf((float)side[i], side_input_scale, t);
+        t = t + bias[k];                 /* (3) bias */
+      }
       t = nearbyintf(t);                 /* round half to even (default mode) */
       if (t < lo) t = lo;                /* clip; ReLU raises the lower bound */
       if (t > hi) t = hi;
       y[i] = (int8_t)t;
     }
   }
+}
+
+void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scale,
+                        const int8_t* side, float side_input_scale,
+                        const float* bias, int relu, int8_t* y) {
+  oracle_epilogue_i8_ex(acc, M, K, conv_input_scale, NULL, side, side_input_scale, bias,
+                        relu, 8, y);
 }
 
 /*

@@ -290,6 +290,54 @@ def test_epilogue_crafted_fma_and_contraction_cases():
         assert int(y[0, 0, 0, 0]) == int(exp), name
 
 
+def test_epilogue_variant_hand_values():
+    """Per-channel scale vectors and the cuDNN 7 order, hand-worked values
+    (tests/golden/epilogue_i8_variants.txt)."""
+    rows = _read_rows("epilogue_i8_variants.txt")
+    assert len(rows) >= 7
+    f32 = lambda t: np.array([float(v) for v in t.split(",")], np.float32)
+    for r in rows:
+        order, relu, sis, accs, scales, biases, sides, exp = r[:8]
+        acc = np.array([int(v) for v in accs.split(",")], np.int32).reshape(1, 1, 1, -1)
+        side = None if sides == "-" else np.array(
+            [int(v) for v in sides.split(",")], np.int8).reshape(acc.shape)
+        y = oracle.epilogue_i8(acc, f32(scales), f32(biases), side, float(sis),
+                               relu == "1", order=int(order))
+        assert y.reshape(-1).tolist() == [int(v) for v in exp.split(",")], r
+
+
+def test_epilogue_cudnn7_order_fuses_scale_and_bias():
+    """Crafted case T2 (epilogue_i8_crafted.txt) rounds differently when scale
+    and bias are one fused multiply-add: 0 in the cuDNN 8 order, 1 in the
+    cuDNN 7 order (5 * 838860.9375 - 4194304 = 0.6875 exactly)."""
+    for name, C, xv, wv, cis, side, sis, bias, relu, exp in _read_rows(
+            "epilogue_i8_crafted.txt"):
+        if name != "T2":
+            continue
+        x = np.full((1, 1, 1, int(C)), int(xv), np.int8)
+        w = np.full((1, 1, int(C), 1), int(wv), np.int8)
+        b = np.array([float(bias)], np.float32)
+        y8 = oracle.fused_conv_i8(x, w, b, np.float32(float(cis)), padding="VALID", order=8)
+        y7 = oracle.fused_conv_i8(x, w, b, np.float32(float(cis)), padding="VALID", order=7)
+        assert int(y8[0, 0, 0, 0]) == int(exp) == 0
+        assert int(y7[0, 0, 0, 0]) == 1
+
+
+def test_per_channel_scale_of_equal_values_is_the_scalar():
+    rng = np.random.default_rng(14)
+    x = wl.draw_int8(rng, (2, 7, 6, 24))
+    w = wl.draw_int8(rng, (3, 3, 24, 20))
+    side = wl.draw_int8(rng, (2, 7, 6, 20))
+    acc = oracle.conv_acc(x, w, 1, "SAME")
+    bias = rng.normal(0, 16, size=20).astype(np.float32)
+    for order in (7, 8):
+        for cis in (np.float32(2.0 ** -11), np.float32(0.0123)):
+            ys = oracle.epilogue_i8(acc, cis, bias, side, 0.25, True, order)
+            yv = oracle.epilogue_i8(acc, np.full(20, cis, np.float32), bias, side, 0.25,
+                                    True, order)
+            np.testing.assert_array_equal(ys, yv)
+
+
 def _round_f32(q: Fraction) -> Fraction:
     """Exact value of the binary32 nearest to q (ties to even), from scratch."""
     if q == 0:
@@ -306,12 +354,17 @@ def _round_f32(q: Fraction) -> Fraction:
     return v if q > 0 else -v
 
 
-def _epilogue_exact(acc, cis, side, sis, bias, relu):
+def _epilogue_exact(acc, cis, side, sis, bias, relu, order=8):
     t = _round_f32(Fraction(int(acc)))
-    t = _round_f32(t * Fraction(float(cis)))
-    if side is not None and sis != 0:
-        t = _round_f32(Fraction(int(side)) * Fraction(float(sis)) + t)
-    t = _round_f32(t + Fraction(float(bias)))
+    if order == 7:
+        t = _round_f32(t * Fraction(float(cis)) + Fraction(float(bias)))
+        if side is not None and sis != 0:
+            t = _round_f32(Fraction(int(side)) * Fraction(float(sis)) + t)
+    else:
+        t = _round_f32(t * Fraction(float(cis)))
+        if side is not None and sis != 0:
+            t = _round_f32(Fraction(int(side)) * Fraction(float(sis)) + t)
+        t = _round_f32(t + Fraction(float(bias)))
     v = round(t)  # half to even
     lo = 0 if relu else -128
     return max(lo, min(127, v))
@@ -340,6 +393,32 @@ def test_epilogue_against_exact_rational_model():
             exp = [_epilogue_exact(acc[i], cis, side[i] if with_side else None, sis,
                                    bias[i], relu) for i in range(n)]
             np.testing.assert_array_equal(y, np.array(exp, np.int8))
+
+
+def test_epilogue_variants_against_exact_rational_model():
+    """Both orders with a per-channel scale vector: the oracle's fp32 steps
+    equal exact rational arithmetic rounded to binary32 at each step (in the
+    cuDNN 7 order, scale and bias round once together)."""
+    rng = np.random.default_rng(15)
+    K, P = 16, 150
+    acc = rng.integers(-2 ** 26, 2 ** 26, size=(P, K)).astype(np.int32)
+    acc[: P // 3] = rng.integers(-600, 600, size=(P // 3, K))
+    side = wl.draw_int8(rng, (P, K), -128, 127)
+    scales = rng.choice([2.0 ** -8, 0.0123, 1 / 3, 2.0 ** -11, 0.7071], size=K).astype(np.float32)
+    scales[0] = np.float32(838860.9375) / np.float32(2.0 ** 20)
+    bias = rng.normal(0, 40, size=K).astype(np.float32)
+    bias[: K // 4] = np.round(bias[: K // 4] * 2) / 2
+    sis = np.float32(0.377)
+    for order in (7, 8):
+        for relu in (False, True):
+            for with_side in (False, True):
+                y = oracle.epilogue_i8(acc.reshape(1, 1, P, K), scales, bias,
+                                       side.reshape(1, 1, P, K) if with_side else None,
+                                       sis, relu, order).reshape(P, K)
+                exp = [[_epilogue_exact(acc[p, k], scales[k], side[p, k] if with_side else None,
+                                        sis, bias[k], relu, order) for k in range(K)]
+                       for p in range(P)]
+                np.testing.assert_array_equal(y, np.array(exp, np.int8))
 
 
 def test_tie_dense_rounding_is_half_even():
