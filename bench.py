@@ -48,14 +48,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(L) -> int:
+def algorithmic_bytes(L, per_channel_scale=False) -> int:
     """Each tensor once: x, filter, side input, y, per-channel vectors."""
     esize = {"int8": 1, "bf16": 2, "fp32": 4}[L.dtype]
     x = L.N * L.H * L.W * L.C * esize
     w = L.R * L.S * L.C * L.K * esize
     y = L.N * L.Ho * L.Wo * L.K * esize
     side = L.N * L.Ho * L.Wo * L.K if L.has_side else 0
-    nvec = 1 + (4 if L.dtype != "int8" and 4 in L.ops else 0)
+    nvec = 1 + (4 if L.dtype != "int8" and 4 in L.ops else 0) + (1 if per_channel_scale else 0)
     return x + w + y + side + 4 * L.K * nvec
 
 
@@ -73,13 +73,14 @@ def measured_traffic(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(L, inp, seconds: float):
+def cpu_baseline(L, inp, seconds: float, cis=None, order=8):
     import oracle
+    cis = L.conv_input_scale if cis is None else cis
     reps, t0 = 0, time.perf_counter()
     while True:
         acc = oracle.conv_acc(inp.x, inp.w, L.stride, L.padding)
-        y = oracle.epilogue_i8(acc, L.conv_input_scale, inp.bias, inp.side,
-                               L.side_input_scale, L.relu)
+        y = oracle.epilogue_i8(acc, cis, inp.bias, inp.side, L.side_input_scale, L.relu,
+                               order)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
@@ -124,6 +125,11 @@ def main():
     ap.add_argument("--workload", default="resnet_3x3_int8")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-channel-scale", action="store_true",
+                    help="int8: one conv_input_scale per output channel (the layer's scale "
+                         "times a seeded factor in [0.5, 2))")
+    ap.add_argument("--cudnn7-order", action="store_true",
+                    help="int8: the cuDNN 7 epilogue order (fused scale and bias)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the conv, time a plain device-to-device copy of "
                          "BYTES bytes (the reference kernel for counter calibration)")
@@ -147,12 +153,21 @@ def main():
     import workloads as wl
 
     L = wl.LAYERS[args.workload]
+    if (args.per_channel_scale or args.cudnn7_order) and L.dtype != "int8":
+        print("--per-channel-scale and --cudnn7-order apply to int8 layers", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     inp = wl.make_inputs(L)
     names = {wl.OP_SCALE: "scale", wl.OP_SIDE: "side", wl.OP_BIAS: "bias", wl.OP_BN: "bn",
              wl.OP_RELU: "relu"}
     plan = fc.Plan(L.N, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
-                   ops=[names[o] for o in L.ops])
+                   ops=[names[o] for o in L.ops], cudnn7_order=args.cudnn7_order)
+    order = 7 if args.cudnn7_order else 8
+    cis_host = L.conv_input_scale
+    if args.per_channel_scale:
+        rng = np.random.default_rng(1000 + L.seed)
+        cis_host = (np.float32(L.conv_input_scale) *
+                    rng.uniform(0.5, 2.0, size=L.K)).astype(np.float32)
 
     def put(a):
         if a is None:
@@ -163,6 +178,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     x, w, bias, side = put(inp.x), put(inp.w), put(inp.bias), put(inp.side)
+    cis = put(cis_host) if args.per_channel_scale else L.conv_input_scale
     bn = None
     if inp.bn is not None:
         bn = {k: put(np.asarray(inp.bn[k], np.float32)) for k in ("gamma", "beta", "mean", "var")}
@@ -173,10 +189,10 @@ def main():
     stream = torch.cuda.current_stream()
     plan.pack_filter(w, ws, stream)
     run_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
-                              conv_input_scale=L.conv_input_scale,
+                              conv_input_scale=cis,
                               side_input_scale=L.side_input_scale, bn=bn, prepacked=True)
     full_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
-                               conv_input_scale=L.conv_input_scale,
+                               conv_input_scale=cis,
                                side_input_scale=L.side_input_scale, bn=bn, prepacked=False)
     h = stream.cuda_stream
 
@@ -251,8 +267,10 @@ def main():
 
     ops = L.ops_count()
     value = ops * args.steps / wall / 1e12
-    alg_bytes = algorithmic_bytes(L)
-    traffic = measured_traffic(L.name, plan.kernel_name)
+    alg_bytes = algorithmic_bytes(L, args.per_channel_scale)
+    # The committed counters were taken with the default epilogue.
+    traffic = (None if args.per_channel_scale or args.cudnn7_order
+               else measured_traffic(L.name, plan.kernel_name))
     # Bound: the roofline the layer meets first (ridge = peak ops / peak bytes).
     ridge = PEAK_TOPS[L.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ops / alg_bytes <= ridge:
@@ -281,6 +299,9 @@ def main():
                    "C": L.C, "K": L.K, "R": L.R, "S": L.S, "stride": L.stride,
                    "padding": L.padding, "filter": "prepacked once per plan",
                    "kernel": plan.kernel_name},
+        "epilogue": ("cuDNN %d order, %s conv_input_scale" %
+                     (order, "per-channel" if args.per_channel_scale else "scalar")
+                     if L.dtype == "int8" else "bias, batch norm, ReLU"),
         "launch": "hip graph of the K steps, replayed once",
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TOPS[L.dtype], 3),
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
@@ -295,7 +316,7 @@ def main():
                          algorithmic_bytes_per_launch=alg_bytes),
     }
     if not args.no_cpu_baseline and L.dtype == "int8":
-        y_ref, cb = cpu_baseline(L, inp, args.cpu_seconds)
+        y_ref, cb = cpu_baseline(L, inp, args.cpu_seconds, cis_host, order)
         cb["sample_matches_gpu"] = bool(np.array_equal(y_ref, y_gpu.numpy()))
         out["cpu_baseline"] = cb
     else:

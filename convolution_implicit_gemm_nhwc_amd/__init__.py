@@ -61,7 +61,7 @@ class Plan:
     """A resolved fused-conv plan (geometry, dtype, ordered epilogue ops)."""
 
     def __init__(self, N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="int8",
-                 ops=("scale", "bias")):
+                 ops=("scale", "bias"), cudnn7_order=False):
         sh, sw = (stride, stride) if isinstance(stride, int) else stride
         d = _abi.FconvDesc()
         d.N, d.H, d.W, d.C, d.K, d.R, d.S = N, H, W, C, K, R, S
@@ -74,7 +74,7 @@ class Plan:
         d.n_ops = len(codes)
         for i, c in enumerate(codes):
             d.ops[i] = c
-        d.flags = 0
+        d.flags = _abi.FCONV_DESC_CUDNN7_ORDER if cudnn7_order else 0
         self.desc = d
         self.dtype = dtype
         self._h = ctypes.c_void_p()
@@ -120,7 +120,14 @@ class Plan:
                                if hasattr(workspace, "numel") else self.workspace_bytes)
         a.workspace_bytes = workspace_bytes
         a.bias, a.side = _addr(bias), _addr(side)
-        a.conv_input_scale = conv_input_scale
+        if hasattr(conv_input_scale, "data_ptr"):
+            # One fp32 value per output channel, on the GPU.
+            if conv_input_scale.numel() != self.desc.K or str(conv_input_scale.dtype) != "torch.float32":
+                raise ValueError("a conv_input_scale tensor needs K fp32 values")
+            a.conv_input_scales = _addr(conv_input_scale)
+            a.conv_input_scale = 0.0
+        else:
+            a.conv_input_scale = conv_input_scale
         a.side_input_scale = side_input_scale
         if bn is not None:
             a.bn_gamma, a.bn_beta = _addr(bn["gamma"]), _addr(bn["beta"])

@@ -18,6 +18,7 @@ FCONV_PAD_SAME, FCONV_PAD_VALID = 0, 1
 OP_SCALE, OP_SIDE, OP_BIAS, OP_BN, OP_RELU = 1, 2, 3, 4, 5
 FCONV_MAX_OPS = 8
 FCONV_RUN_FILTER_PREPACKED = 1
+FCONV_DESC_CUDNN7_ORDER = 1
 
 # Every symbol include/fconv.h declares.
 EXPORTS = ("fconv_plan_create", "fconv_plan_output_dims", "fconv_plan_workspace_size",
@@ -39,7 +40,8 @@ class FconvArgs(ctypes.Structure):
                 ("bn_beta", ctypes.c_void_p), ("bn_mean", ctypes.c_void_p),
                 ("bn_var", ctypes.c_void_p), ("bn_eps", ctypes.c_float),
                 ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32),
+                ("conv_input_scales", ctypes.c_void_p)]
 
 
 class LibraryMissing(RuntimeError):

@@ -119,6 +119,8 @@ struct ConvArgs {
   // m / Wo and q / Ho by multiply-high: q = (umulhi(n, mul) + (add ? n : 0)) >> shift
   uint32_t wo_mul, wo_add, wo_shift, ho_mul, ho_add, ho_shift;
   int32_t use_side, use_bias, use_bn, relu;
+  const float* cis_vec;  // per-channel conv_input_scale [K], or null: cis for all
+  int32_t cudnn7;        // int8 epilogue in the cuDNN 7 order
   // Row-halo kernel: output rows per workgroup and rows of its first phase
   // (set by its launcher).
   int32_t halo_rows, halo_rows_a;
@@ -201,10 +203,21 @@ __device__ inline void load_bias(const ConvArgs& a, int ch0, bool kvec, float (&
   }
 }
 
+// The conv_input_scale of a lane's NCH channels: the per-channel vector
+// (0 past K) or the scalar.
+template <int NCH>
+__device__ inline void load_scales(const ConvArgs& a, int ch0, bool kvec, float (&cis)[NCH]) {
+#pragma unroll
+  for (int e = 0; e < NCH; ++e) {
+    const int ch = ch0 + e;
+    cis[e] = a.cis_vec ? ((kvec || ch < a.K) ? a.cis_vec[ch] : 0.0f) : a.cis;
+  }
+}
+
 template <int NCH = 16>
 __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs& a,
                                          int m, int ch0, bool kvec, i32x4 side_chunk,
-                                         const float (&bias)[NCH]) {
+                                         const float (&bias)[NCH], const float (&cis)[NCH]) {
   int8_t* y = static_cast<int8_t*>(a.y) + static_cast<int64_t>(m) * a.K + ch0;
   union {
     int8_t b[16];
@@ -217,9 +230,15 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
   for (int e = 0; e < NCH; ++e) {
     const float b = bias[e];
     float t = static_cast<float>(v[e]);        // int32 -> fp32, nearest even
-    t = t * a.cis;                             // (1) scale
-    if (a.use_side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);  // (2)
-    t = t + b;                                 // (3) bias
+    if (a.cudnn7) {
+      // cuDNN 7 order: scale and bias in one fused multiply-add, then side.
+      t = __builtin_fmaf(t, cis[e], b);
+      if (a.use_side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);
+    } else {
+      t = t * cis[e];                          // (1) scale
+      if (a.use_side) t = __builtin_fmaf(static_cast<float>(s.b[e]), a.sis, t);  // (2)
+      t = t + b;                               // (3) bias
+    }
     t = __builtin_rintf(t);                    // round half to even
     t = __builtin_fminf(__builtin_fmaxf(t, lo), 127.0f);
     o.b[e] = static_cast<int8_t>(static_cast<int32_t>(t));
@@ -239,9 +258,10 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
 template <int NCH = 16>
 __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs& a,
                                          int m, int ch0, bool kvec, i32x4 side_chunk) {
-  float bias[NCH];
+  float bias[NCH], cis[NCH];
   load_bias<NCH>(a, ch0, kvec, bias);
-  epilogue_store_i8<NCH>(v, a, m, ch0, kvec, side_chunk, bias);
+  load_scales<NCH>(a, ch0, kvec, cis);
+  epilogue_store_i8<NCH>(v, a, m, ch0, kvec, side_chunk, bias, cis);
 }
 
 // bf16 / fp32: bias -> batch-norm inference -> ReLU (MIOpen's CBNA order).
@@ -704,15 +724,16 @@ void conv_tile_kernel(ConvArgs a) {
   // during the main loop (and no later than the first stage's copies).
   const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
   const bool ch_live = ch0 < a.K;
-  float bias_pre[8];
+  float bias_pre[8], cis_pre[8];
   i32x4 side_pre[4];
   FloatEpiParams<8> fpar;
   if constexpr (DT == FCONV_INT8) {
     if (ch_live) {
       load_bias<8>(a, ch0, KVEC, bias_pre);
+      load_scales<8>(a, ch0, KVEC, cis_pre);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bias_pre[e] = 0.0f;
+      for (int e = 0; e < 8; ++e) bias_pre[e] = cis_pre[e] = 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -860,7 +881,7 @@ void conv_tile_kernel(ConvArgs a) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      epilogue_store_i8<8>(v, a, m, ch0, KVEC, side_pre[i], bias_pre);
+      epilogue_store_i8<8>(v, a, m, ch0, KVEC, side_pre[i], bias_pre, cis_pre);
     }
   } else {
 #pragma unroll
@@ -938,7 +959,7 @@ __device__ inline void store_words(const uint32_t (&w)[NOUT / 4], __amdgpu_buffe
 //   magic + 1.5 * 2^23 (round half to even)
 //   med3  clip
 //   pack  byte packing into NOUT/4 words
-template <bool SIDE, int NOUT>
+template <bool SIDE, int NOUT, bool ORDER7 = false>
 struct EpiI8 {
   static constexpr int kCvt = NOUT / 8;
   static constexpr int kSide = SIDE ? NOUT / 8 : 0;
@@ -947,8 +968,8 @@ struct EpiI8 {
   uint32_t w[NOUT / 4];
 
   __device__ inline void stage(int st, const i32x4 (&acc)[NOUT / 4], i32x4 side_chunk,
-                               const float (&bias)[NOUT], float cis, float sis, float lo_b,
-                               float hi_b) {
+                               const float (&bias)[NOUT], const float (&cis)[NOUT], float sis,
+                               float lo_b, float hi_b) {
     union {
       int8_t b[16];
       i32x4 v;
@@ -962,7 +983,12 @@ struct EpiI8 {
     st -= kCvt;
     if (st == 0) {
 #pragma unroll
-      for (int e = 0; e < NOUT; ++e) t[e] = t[e] * cis;
+      for (int e = 0; e < NOUT; ++e) {
+        if constexpr (ORDER7)
+          t[e] = __builtin_fmaf(t[e], cis[e], bias[e]);  // cuDNN 7: scale and bias fused
+        else
+          t[e] = t[e] * cis[e];
+      }
       return;
     }
     st -= 1;
@@ -975,8 +1001,10 @@ struct EpiI8 {
     st -= kSide;
     switch (st) {
       case 0:
+        if constexpr (!ORDER7) {
 #pragma unroll
-        for (int e = 0; e < NOUT; ++e) t[e] = t[e] + bias[e];
+          for (int e = 0; e < NOUT; ++e) t[e] = t[e] + bias[e];
+        }
         break;
       case 1:
 #pragma unroll
@@ -1011,14 +1039,15 @@ struct EpiI8 {
 
 // Whole int8 epilogue of one tile for this lane's pixel and NOUT channels,
 // written with one buffer store; an out-of-range offset drops it.
-template <bool SIDE, int NOUT>
+template <bool SIDE, int NOUT, bool ORDER7 = false>
 __device__ inline void stream_epilogue_i8(const i32x4 (&acc)[NOUT / 4], i32x4 side_chunk,
-                                          const float (&bias)[NOUT], float cis, float sis,
+                                          const float (&bias)[NOUT], const float (&cis)[NOUT],
+                                          float sis,
                                           float lo_b, float hi_b, __amdgpu_buffer_rsrc_t yr,
                                           uint32_t off) {
-  EpiI8<SIDE, NOUT> ep;
+  EpiI8<SIDE, NOUT, ORDER7> ep;
 #pragma unroll
-  for (int st = 0; st < EpiI8<SIDE, NOUT>::kStages; ++st)
+  for (int st = 0; st < EpiI8<SIDE, NOUT, ORDER7>::kStages; ++st)
     ep.stage(st, acc, side_chunk, bias, cis, sis, lo_b, hi_b);
   store_words<NOUT>(ep.w, yr, off);
 }
@@ -1035,7 +1064,7 @@ __device__ inline void stream_epilogue_i8(const i32x4 (&acc)[NOUT / 4], i32x4 si
 // k-steps are buffer loads issued two tiles ahead; a tap outside the image
 // gets an offset past the extent and reads zeros.  Offsets use 24-bit
 // multiplies (every operand and product here is far below 2^24 / 2^31).
-template <int R, int S, int CS, bool SIDE, int KSPLIT>
+template <int R, int S, int CS, bool SIDE, int KSPLIT, bool ORDER7>
 __global__ __launch_bounds__(256 * KSPLIT) __attribute__((amdgpu_waves_per_eu(KSPLIT, KSPLIT)))
 void conv_stream_i8_kernel(ConvArgs a) {
   constexpr int NKS = R * S * CS;
@@ -1159,7 +1188,23 @@ void conv_stream_i8_kernel(ConvArgs a) {
     bias[4 * q + 2] = v.z;
     bias[4 * q + 3] = v.w;
   }
-  const float cis = a.cis, sis = a.sis;
+  float cis[NOUT];
+  if (a.cis_vec) {
+    const __amdgpu_buffer_rsrc_t cr = make_rsrc(a.cis_vec, static_cast<uint32_t>(a.K) * 4u);
+#pragma unroll
+    for (int q = 0; q < NOUT / 4; ++q) {
+      const f32x4 v = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, static_cast<uint32_t>((ch0 + 4 * q) * 4), 0, 0));
+      cis[4 * q] = v.x;
+      cis[4 * q + 1] = v.y;
+      cis[4 * q + 2] = v.z;
+      cis[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < NOUT; ++e) cis[e] = a.cis;
+  }
+  const float sis = a.sis;
   const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt = expcnt = lgkmcnt = 0
   __syncthreads();
@@ -1184,10 +1229,10 @@ void conv_stream_i8_kernel(ConvArgs a) {
                   int k_load, uint32_t off_prev) {
     uint32_t o[NKS];
     offsets(k_load, o);
-    EpiI8<SIDE, NOUT> ep;
+    EpiI8<SIDE, NOUT, ORDER7> ep;
 #pragma unroll
     for (int j = 0; j < NOUT / 4; ++j) ep.w[j] = 0u;
-    constexpr int NS = EpiI8<SIDE, NOUT>::kStages;
+    constexpr int NS = EpiI8<SIDE, NOUT, ORDER7>::kStages;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -1217,7 +1262,7 @@ void conv_stream_i8_kernel(ConvArgs a) {
     half(bB, accB, accA, sA, k + 3, out_off(k));
     sA = issue_side(k + 2);
   }
-  stream_epilogue_i8<SIDE, NOUT>(accB, sB, bias, cis, sis, lo_b, hi_b, yr, out_off(k - 1));
+  stream_epilogue_i8<SIDE, NOUT, ORDER7>(accB, sB, bias, cis, sis, lo_b, hi_b, yr, out_off(k - 1));
 }
 
 // ------------------------------------------------------------- row-halo int8
@@ -1309,7 +1354,7 @@ __device__ inline void wait_vmcnt_at_most(int n) {
   }
 }
 
-template <int R, int S, bool SIDE>
+template <int R, int S, bool SIDE, bool ORDER7>
 __global__ __launch_bounds__(kHaloThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_halo_i8_kernel(ConvArgs a) {
   constexpr int NKS = R * S;
@@ -1321,7 +1366,10 @@ void conv_halo_i8_kernel(ConvArgs a) {
   // Accumulator hand-off, per MFMA wave and step parity: chunk q (accumulator
   // tile q, 4 int32) of lane l at q * 1024 + 16 * l.
   __shared__ __attribute__((aligned(256))) char accb[4 * 2 * 4096];
-  __shared__ __attribute__((aligned(16))) float blds[256];  // the slice's 64 bias values
+  // The slice's 64 bias values and per-channel scales (a copy's 64 lanes
+  // write 1 KiB: lanes past the 16 that carry values write zeros).
+  __shared__ __attribute__((aligned(16))) float blds[256];
+  __shared__ __attribute__((aligned(16))) float clds[256];
 
   const int lane = threadIdx.x & 63;
   // readfirstlane: the wave index (and so the role) is uniform per wave.
@@ -1437,6 +1485,10 @@ void conv_halo_i8_kernel(ConvArgs a) {
         const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
                                        : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
+        if (a.cis_vec)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              make_rsrc(a.cis_vec, static_cast<uint32_t>(a.K) * 4u), (lds_ptr_t)clds, 16, off, 0,
+              0, 0);
       } else {
         copy_rows(PB, xb, i - 1);
       }
@@ -1530,7 +1582,10 @@ void conv_halo_i8_kernel(ConvArgs a) {
     float bias[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias[e] = blds[16 * g + e];
-    const float cis = a.cis, sis = a.sis;
+    float cis[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cis[e] = a.cis_vec ? clds[16 * g + e] : a.cis;
+    const float sis = a.sis;
     const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
     auto epi_phase = [&](const HaloPhase& P, int steps, int step0) {
       for (int ls = 0; ls < steps; ++ls) {
@@ -1567,7 +1622,7 @@ void conv_halo_i8_kernel(ConvArgs a) {
         }
         const bool ok = p < P.npx && ch0 < a.K;
         const uint32_t off = ok ? static_cast<uint32_t>((P.p0 * a.Wo + p) * a.K + ch0) : kOutOfRange;
-        stream_epilogue_i8<SIDE, 16>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
+        stream_epilogue_i8<SIDE, 16, ORDER7>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
         if constexpr (SIDE) copy_side(t + 2);  // into the slot step t - 1 read
         if (t == 0 && sA >= 2) __builtin_amdgcn_s_waitcnt(SIDE ? 0x0f72 : 0x0f71);  // phase B's rows
         barrier();
@@ -1658,10 +1713,14 @@ hipError_t launch_stream_shape(const fconv_plan_s* p, const ConvArgs& a, hipStre
   if (grid > cus) grid = cus;
   const dim3 g(static_cast<unsigned>(grid), static_cast<unsigned>(p->Kp / 64));
   const size_t lds = static_cast<size_t>(64) * a.wrow_bytes;
-  if (a.use_side)
-    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true, 1>), g, dim3(kThreads), lds, s, a);
+  if (a.use_side && a.cudnn7)
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true, 1, true>), g, dim3(kThreads), lds, s, a);
+  else if (a.use_side)
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, true, 1, false>), g, dim3(kThreads), lds, s, a);
+  else if (a.cudnn7)
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false, 1, true>), g, dim3(kThreads), lds, s, a);
   else
-    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false, 1>), g, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((conv_stream_i8_kernel<R, S, CS, false, 1, false>), g, dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -1714,10 +1773,14 @@ hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStrea
   a.halo_rows = rows;
   a.halo_rows_a = std::min(kHaloRowsA, rows);
   const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows), static_cast<unsigned>(p->Kp / 64));
-  if (a.use_side)
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true>), g, dim3(kHaloThreads), 0, s, a);
+  if (a.use_side && a.cudnn7)
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true, true>), g, dim3(kHaloThreads), 0, s, a);
+  else if (a.use_side)
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true, false>), g, dim3(kHaloThreads), 0, s, a);
+  else if (a.cudnn7)
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false, true>), g, dim3(kHaloThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false>), g, dim3(kHaloThreads), 0, s, a);
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false, false>), g, dim3(kHaloThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1799,6 +1862,8 @@ fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) 
   a.bn_var = args->bn_var;
   a.y = args->y;
   a.cis = args->conv_input_scale;
+  a.cis_vec = args->conv_input_scales;
+  a.cudnn7 = p->cudnn7;
   a.sis = args->side_input_scale;
   a.bn_eps = args->bn_eps;
   a.N = p->d.N; a.H = p->d.H; a.W = p->d.W; a.C = p->d.C; a.K = p->d.K;

@@ -201,15 +201,17 @@ fconv_status check_run_args(const fconv_plan_s* p, const fconv_args* a) {
   if (p->op_side && !a->side) return FCONV_ERR_INVALID_ARG;
   if (p->op_bn && (!a->bn_gamma || !a->bn_beta || !a->bn_mean || !a->bn_var))
     return FCONV_ERR_INVALID_ARG;
+  if (a->conv_input_scales && !p->op_scale) return FCONV_ERR_UNSUPPORTED;
   if (!a->workspace || a->workspace_bytes < p->ws_bytes) return FCONV_ERR_WORKSPACE;
   if (!aligned(a->x, 16) || !aligned(a->y, 16) || !aligned(a->workspace, 16) ||
       (!prepacked && !aligned(a->w, 16)) || (p->op_side && !aligned(a->side, 16)))
     return FCONV_ERR_MISALIGNED;
-  const float* vecs[5] = {p->op_bias ? a->bias : nullptr,
+  const float* vecs[6] = {p->op_bias ? a->bias : nullptr,
                           p->op_bn ? a->bn_gamma : nullptr,
                           p->op_bn ? a->bn_beta : nullptr,
                           p->op_bn ? a->bn_mean : nullptr,
-                          p->op_bn ? a->bn_var : nullptr};
+                          p->op_bn ? a->bn_var : nullptr,
+                          a->conv_input_scales};
   for (const float* v : vecs)
     if (v && !aligned(v, 4)) return FCONV_ERR_MISALIGNED;
   // No in-place operation: y may not overlap anything the run reads, nor the
@@ -238,7 +240,8 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
     return FCONV_ERR_UNSUPPORTED;
   if (d.padding != FCONV_PAD_SAME && d.padding != FCONV_PAD_VALID)
     return FCONV_ERR_UNSUPPORTED;
-  if (d.flags != 0) return FCONV_ERR_UNSUPPORTED;
+  if (d.flags & ~FCONV_DESC_CUDNN7_ORDER) return FCONV_ERR_UNSUPPORTED;
+  if ((d.flags & FCONV_DESC_CUDNN7_ORDER) && d.dtype != FCONV_INT8) return FCONV_ERR_UNSUPPORTED;
   if (d.N < 0 || d.H < 1 || d.W < 1 || d.C < 1 || d.K < 1 || d.R < 1 || d.S < 1 ||
       d.stride_h < 1 || d.stride_w < 1)
     return FCONV_ERR_INVALID_ARG;
@@ -246,6 +249,7 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
   fconv_plan_s* p = new (std::nothrow) fconv_plan_s();
   if (!p) return FCONV_ERR_INVALID_ARG;
   p->d = d;
+  p->cudnn7 = (d.flags & FCONV_DESC_CUDNN7_ORDER) != 0;
   const bool same = d.padding == FCONV_PAD_SAME;
   if (!resolve_axis(d.H, d.R, d.stride_h, same, &p->Ho, &p->pt, &p->pb) ||
       !resolve_axis(d.W, d.S, d.stride_w, same, &p->Wo, &p->pl, &p->pr)) {

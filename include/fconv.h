@@ -102,10 +102,19 @@ typedef enum {
 
 #define FCONV_MAX_OPS 8
 
+/* Plan flag (int8 only): the cuDNN 7 order of the int8 epilogue that
+ * TensorFlow conv_ops_fused_int8.cc names in BiasActivationOutputKernel:
+ *     t = fmaf((float)acc, conv_input_scale, bias[k])   one rounding
+ *     t = fmaf((float)side, side_input_scale, t)         (SIDE op)
+ *     y = (int8)clamp(rint(t), RELU ? 0 : -128, 127)
+ * instead of the cuDNN 8 order above. */
+#define FCONV_DESC_CUDNN7_ORDER 1u
+
 /* Geometry and operator sequence of a plan (all by value; copied at create).
  * N may be 0 (every run is then a no-op); H, W, C, K, R, S, strides >= 1.
  * Groups and dilation are always 1 (the fused op on the pages supports no
- * other value). `flags` is reserved and must be 0. */
+ * other value). `flags`: 0 or FCONV_DESC_CUDNN7_ORDER (int8 plans); any
+ * other bit is FCONV_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t N, H, W, C, K, R, S;
   int32_t stride_h, stride_w;
@@ -128,6 +137,10 @@ typedef struct fconv_plan_s* fconv_plan;
  *   bias   device, fp32 [K]                          (needed iff BIAS op)
  *   side   device, int8 NHWC [N][Ho][Wo][K]           (needed iff SIDE op)
  *   conv_input_scale, side_input_scale: fp32 scalars (SCALE / SIDE ops)
+ *   conv_input_scales  NULL, or device fp32 [K]: one conv_input_scale per
+ *          output channel, which replaces the scalar (TensorFlow
+ *          conv_ops_fused_int8.cc slices a scale tensor of more than one
+ *          element at the output channel); int8 plans only
  *   bn_gamma, bn_beta, bn_mean, bn_var: device fp32 [K] (needed iff BN op)
  *   bn_eps: batch-norm epsilon
  *   y      device, NHWC [N][Ho][Wo][K] of the plan dtype; must not overlap
@@ -153,6 +166,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   uint32_t flags;
+  const float* conv_input_scales;
 } fconv_args;
 
 /* Validates `desc`, resolves output size and padding, checks the operator

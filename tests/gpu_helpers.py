@@ -44,9 +44,10 @@ def from_dev(t, dtype):
     return t.cpu().numpy()
 
 
-def make_plan(N, H, W, C, K, R, S, stride, padding, dtype, ops):
+def make_plan(N, H, W, C, K, R, S, stride, padding, dtype, ops, cudnn7_order=False):
     return fc.Plan(N, H, W, C, K, R, S, stride, padding, dtype,
-                   ops=[OPNAMES[o] if isinstance(o, int) else o for o in ops])
+                   ops=[OPNAMES[o] if isinstance(o, int) else o for o in ops],
+                   cudnn7_order=cudnn7_order)
 
 
 def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
@@ -71,7 +72,9 @@ def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
         ws = prepacked_ws
     else:
         ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
-    plan.run(xd, wd, y, ws, bias=bd, side=sd, conv_input_scale=float(cis),
+    # cis: a scalar, or a numpy fp32 vector of one scale per output channel
+    cis_arg = to_dev(np.asarray(cis, np.float32), dev) if np.ndim(cis) > 0 else float(cis)
+    plan.run(xd, wd, y, ws, bias=bd, side=sd, conv_input_scale=cis_arg,
              side_input_scale=float(sis), bn=bnd, prepacked=prepacked_ws is not None)
     torch.cuda.synchronize()
     out = from_dev(y, dtype)
@@ -83,10 +86,11 @@ def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
 
 
 def oracle_out(dtype, x, w, stride, padding, bias=None, side=None, cis=1.0, sis=0.0,
-               relu=False, bn=None, use_bias=True):
+               relu=False, bn=None, use_bias=True, order=8):
     if dtype == "int8":
-        return oracle.fused_conv_i8(x, w, bias, np.float32(cis), side, np.float32(sis), relu,
-                                    stride, padding)
+        c = np.asarray(cis, np.float32) if np.ndim(cis) > 0 else np.float32(cis)
+        return oracle.fused_conv_i8(x, w, bias, c, side, np.float32(sis), relu,
+                                    stride, padding, order=order)
     return oracle.fused_conv_float(x, w, bias if use_bias else None, bn, relu, stride, padding)
 
 

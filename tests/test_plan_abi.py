@@ -87,7 +87,10 @@ def test_operator_sequences(ops, dtype, ok):
 def test_create_rejects_unknown_enums_and_flags():
     assert _create(_desc(dtype=7)) == _abi.FCONV_ERR_UNSUPPORTED
     assert _create(_desc(padding=3)) == _abi.FCONV_ERR_UNSUPPORTED
-    assert _create(_desc(flags=1)) == _abi.FCONV_ERR_UNSUPPORTED
+    assert _create(_desc(flags=2)) == _abi.FCONV_ERR_UNSUPPORTED
+    assert _create(_desc(flags=_abi.FCONV_DESC_CUDNN7_ORDER)) == _abi.FCONV_OK
+    assert _create(_desc(flags=_abi.FCONV_DESC_CUDNN7_ORDER, dtype=1, ops=[3])) == \
+        _abi.FCONV_ERR_UNSUPPORTED
     assert _create(_desc(ops=list(range(9)))) == _abi.FCONV_ERR_INVALID_ARG
     assert _create(_desc(N=2 ** 20, H=2 ** 10, W=2 ** 10, C=4)) == _abi.FCONV_ERR_UNSUPPORTED
 
@@ -211,3 +214,25 @@ def test_python_binding_refuses_host_tensors():
     p = fc.Plan(1, 8, 8, 16, 16, 3, 3)
     with pytest.raises(ValueError):
         p.run(torch.zeros(1, 8, 8, 16, dtype=torch.int8), None, None, None)
+
+
+def test_cudnn7_plans_choose_the_same_kernel_family():
+    """Every int8 kernel family implements both epilogue orders, so the flag
+    does not change the kernel choice."""
+    shapes = [(32, 56, 56, 64, 64, 3, 3, 1), (32, 56, 56, 256, 64, 1, 1, 1),
+              (64, 56, 56, 128, 128, 3, 3, 2), (1, 8, 8, 8, 8, 3, 3, 1)]
+    for N, H, W, C, K, R, S, st in shapes:
+        p8 = fc.Plan(N, H, W, C, K, R, S, st, "SAME", "int8", INT8_OPS)
+        p7 = fc.Plan(N, H, W, C, K, R, S, st, "SAME", "int8", INT8_OPS, cudnn7_order=True)
+        assert p7.kernel_name == p8.kernel_name
+
+
+def test_run_checks_per_channel_scales():
+    p, (x, w, y, wsp), kw, ws = _plan_and_args()
+    a = p.make_args(x, w, y, wsp, workspace_bytes=ws, **kw)
+    a.conv_input_scales = FAKE + 2 ** 25 + 2  # not 4-byte aligned
+    assert p.run_args(a, stream=0) == _abi.FCONV_ERR_MISALIGNED
+    pf = fc.Plan(2, 8, 8, 16, 16, 3, 3, 1, "SAME", "fp32", ["bias"])
+    af = pf.make_args(x, w, y, wsp, workspace_bytes=pf.workspace_bytes, bias=kw["bias"])
+    af.conv_input_scales = FAKE + 2 ** 25
+    assert pf.run_args(af, stream=0) == _abi.FCONV_ERR_UNSUPPORTED
