@@ -68,6 +68,10 @@ def _load():
         lib.oracle_epilogue_float.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
                                               ctypes.c_float, i, p]
         lib.oracle_epilogue_float.restype = None
+        lib.oracle_epilogue_float_ex.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
+                                                 ctypes.c_float, i, ctypes.c_float,
+                                                 ctypes.c_float, p]
+        lib.oracle_epilogue_float_ex.restype = None
         lib.oracle_num_threads.restype = i
         _lib = lib
     return _lib
@@ -179,11 +183,20 @@ def epilogue_i8(acc, conv_input_scale, bias, side=None, side_input_scale=0.0,
     return y
 
 
-def epilogue_float(acc, bias=None, bn=None, relu=False):
-    """bias -> batch-norm inference -> ReLU in double.
+ACTIVATIONS = {None: 0, "relu": 1, "leaky_relu": 2, "clipped_relu": 3, "clamp": 4}
 
-    bn = dict(gamma=, beta=, mean=, var=, eps=) or None.
+
+def epilogue_float(acc, bias=None, bn=None, relu=False, act=None, alpha=0.0, beta=0.0):
+    """bias -> batch-norm inference -> activation in double.
+
+    bn = dict(gamma=, beta=, mean=, var=, eps=) or None.  The activation is
+    `act` (None, "relu", "leaky_relu", "clipped_relu", "clamp") with its
+    arguments alpha and beta; relu=True is act="relu".
     """
+    if relu:
+        act = act or "relu"
+    if act not in ACTIVATIONS:
+        raise OracleError("unknown activation %r" % (act,))
     acc = np.ascontiguousarray(acc, dtype=np.float64)
     K = acc.shape[-1]
     M = acc.size // K
@@ -196,8 +209,9 @@ def epilogue_float(acc, bias=None, bn=None, relu=False):
         g = b = mu = var = None
         eps = 0.0
     y = np.empty(acc.shape, dtype=np.float64)
-    _load().oracle_epilogue_float(_ptr(acc), M, K, _ptr(bias), _ptr(g), _ptr(b),
-                                  _ptr(mu), _ptr(var), eps, int(bool(relu)), _ptr(y))
+    _load().oracle_epilogue_float_ex(_ptr(acc), M, K, _ptr(bias), _ptr(g), _ptr(b),
+                                     _ptr(mu), _ptr(var), eps, ACTIVATIONS[act], float(alpha),
+                                     float(beta), _ptr(y))
     return y
 
 
@@ -208,9 +222,9 @@ def fused_conv_i8(x, w, bias, conv_input_scale, side=None, side_input_scale=0.0,
 
 
 def fused_conv_float(x, w, bias=None, bn=None, relu=False, stride=1,
-                     padding="SAME"):
+                     padding="SAME", act=None, alpha=0.0, beta=0.0):
     acc = conv_acc(x, w, stride, padding)
-    return epilogue_float(acc, bias, bn, relu)
+    return epilogue_float(acc, bias, bn, relu, act, alpha, beta)
 
 
 def num_threads():

@@ -55,7 +55,12 @@
  *    the order they are added, and the supported-fusion tables list
  *    conv -> bias -> batch-norm inference -> activation (CBNA).  Batch-norm
  *    inference is the standard gamma * (t - mean) / sqrt(var + eps) + beta,
- *    evaluated here unfolded, in double.
+ *    evaluated here unfolded, in double.  The activation is ReLU or one of the
+ *    other modes the same page's fusion tables list for these combinations:
+ *    Leaky Relu, Clipped Relu and CLAMP, with the activation arguments alpha
+ *    and beta (miopenSetOpArgsActivForward).  The page names them without
+ *    formulas; read plainly: leaky t > 0 ? t : alpha * t; clipped
+ *    min(max(t, 0), alpha); clamp min(max(t, alpha), beta).
  */
 #include <math.h>
 #include <stdint.h>
@@ -361,10 +366,17 @@ void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scal
  * in that order, in double.  bias == NULL skips the bias; gamma == NULL skips
  * the batch norm (then beta/mean/var are ignored).
  */
-void oracle_epilogue_float(const double* acc, long M, int K, const float* bias,
-                           const float* gamma, const float* beta,
-                           const float* mean, const float* var, float eps,
-                           int relu, double* y) {
+/* Activation modes of the float epilogue. */
+#define ORACLE_ACT_NONE 0
+#define ORACLE_ACT_RELU 1
+#define ORACLE_ACT_LEAKY 2
+#define ORACLE_ACT_CLIPPED 3
+#define ORACLE_ACT_CLAMP 4
+
+void oracle_epilogue_float_ex(const double* acc, long M, int K, const float* bias,
+                              const float* gamma, const float* beta,
+                              const float* mean, const float* var, float eps,
+                              int act, float alpha, float act_beta, double* y) {
 #pragma omp parallel for schedule(static)
   for (long m = 0; m < M; ++m) {
     for (int k = 0; k < K; ++k) {
@@ -375,10 +387,35 @@ void oracle_epilogue_float(const double* acc, long M, int K, const float* bias,
         t = (double)gamma[k] * (t - (double)mean[k]) /
                 sqrt((double)var[k] + (double)eps) +
             (double)beta[k];
-      if (relu && t < 0.0) t = 0.0;
+      switch (act) {
+        case ORACLE_ACT_RELU:
+          if (t < 0.0) t = 0.0;
+          break;
+        case ORACLE_ACT_LEAKY:
+          if (!(t > 0.0)) t = (double)alpha * t;
+          break;
+        case ORACLE_ACT_CLIPPED:
+          if (t < 0.0) t = 0.0;
+          if (t > (double)alpha) t = (double)alpha;
+          break;
+        case ORACLE_ACT_CLAMP:
+          if (t < (double)alpha) t = (double)alpha;
+          if (t > (double)act_beta) t = (double)act_beta;
+          break;
+        default:
+          break;
+      }
       y[i] = t;
     }
   }
+}
+
+void oracle_epilogue_float(const double* acc, long M, int K, const float* bias,
+                           const float* gamma, const float* beta,
+                           const float* mean, const float* var, float eps,
+                           int relu, double* y) {
+  oracle_epilogue_float_ex(acc, M, K, bias, gamma, beta, mean, var, eps,
+                           relu ? ORACLE_ACT_RELU : ORACLE_ACT_NONE, 0.0f, 0.0f, y);
 }
 
 int oracle_num_threads(void) {

@@ -462,6 +462,44 @@ def test_float_epilogue_against_torch_batch_norm():
                                   acc + bias.astype(np.float64))
 
 
+@pytest.mark.parametrize("act,alpha,beta", [
+    ("leaky_relu", 0.1, 0.0), ("leaky_relu", 0.0, 0.0), ("clipped_relu", 0.75, 0.0),
+    ("clamp", -0.4, 0.6)])
+def test_float_activations_against_torch(act, alpha, beta):
+    """bias -> batch norm -> activation equals torch's eval-mode batch_norm
+    followed by torch's own leaky_relu / hardtanh(0, alpha) / clamp, in
+    float64, on data that crosses every threshold."""
+    rng = np.random.default_rng(16)
+    K = 10
+    acc = rng.standard_normal((2, 5, 3, K)) * 2
+    acc[0, 0, 0, :4] = [0.0, -0.0, alpha, beta]  # values on the thresholds
+    bias = rng.normal(0, 0.1, K).astype(np.float32)
+    bn = dict(mean=rng.normal(0, 0.1, K).astype(np.float32),
+              var=rng.uniform(0.5, 1.5, K).astype(np.float32),
+              gamma=rng.uniform(0.5, 1.5, K).astype(np.float32),
+              beta=rng.normal(0, 0.1, K).astype(np.float32), eps=1e-5)
+    for with_bn in (False, True):
+        y = oracle.epilogue_float(acc, bias, bn if with_bn else None, act=act, alpha=alpha,
+                                  beta=beta)
+        t = torch.from_numpy(acc + bias.astype(np.float64)).permute(0, 3, 1, 2)
+        if with_bn:
+            t = F.batch_norm(t, torch.from_numpy(bn["mean"]).double(),
+                             torch.from_numpy(bn["var"]).double(),
+                             torch.from_numpy(bn["gamma"]).double(),
+                             torch.from_numpy(bn["beta"]).double(), training=False,
+                             eps=bn["eps"])
+        a32 = float(np.float32(alpha))
+        b32 = float(np.float32(beta))
+        if act == "leaky_relu":
+            ref = F.leaky_relu(t, negative_slope=a32)
+        elif act == "clipped_relu":
+            ref = F.hardtanh(t, 0.0, a32)
+        else:
+            ref = torch.clamp(t, a32, b32)
+        ref = ref.permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
 def test_workload_accumulators_fit_int32():
     """The largest possible |acc| of the strided layer (127*127*1152) exceeds
     2^24 but fits int32; the oracle flags sums outside int32."""
