@@ -130,6 +130,9 @@ def main():
                          "times a seeded factor in [0.5, 2))")
     ap.add_argument("--cudnn7-order", action="store_true",
                     help="int8: the cuDNN 7 epilogue order (fused scale and bias)")
+    ap.add_argument("--activation", default=None, metavar="NAME[:ALPHA[:BETA]]",
+                    help="bf16/fp32: replace the layer's ReLU by leaky_relu, clipped_relu or "
+                         "clamp with these arguments")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the conv, time a plain device-to-device copy of "
                          "BYTES bytes (the reference kernel for counter calibration)")
@@ -160,8 +163,18 @@ def main():
     inp = wl.make_inputs(L)
     names = {wl.OP_SCALE: "scale", wl.OP_SIDE: "side", wl.OP_BIAS: "bias", wl.OP_BN: "bn",
              wl.OP_RELU: "relu"}
+    opnames = [names[o] for o in L.ops]
+    act_alpha = act_beta = 0.0
+    if args.activation:
+        if L.dtype == "int8":
+            print("--activation applies to bf16/fp32 layers", file=sys.stderr)
+            sys.exit(2)
+        parts = args.activation.split(":")
+        act_alpha = float(parts[1]) if len(parts) > 1 else 0.0
+        act_beta = float(parts[2]) if len(parts) > 2 else 0.0
+        opnames = [o for o in opnames if o != "relu"] + [parts[0]]
     plan = fc.Plan(L.N, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
-                   ops=[names[o] for o in L.ops], cudnn7_order=args.cudnn7_order)
+                   ops=opnames, cudnn7_order=args.cudnn7_order)
     order = 7 if args.cudnn7_order else 8
     cis_host = L.conv_input_scale
     if args.per_channel_scale:
@@ -190,10 +203,12 @@ def main():
     plan.pack_filter(w, ws, stream)
     run_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
                               conv_input_scale=cis,
-                              side_input_scale=L.side_input_scale, bn=bn, prepacked=True)
+                              side_input_scale=L.side_input_scale, bn=bn, prepacked=True,
+                              activ_alpha=act_alpha, activ_beta=act_beta)
     full_args = plan.make_args(x, w, y, ws, bias=bias, side=side,
                                conv_input_scale=cis,
-                               side_input_scale=L.side_input_scale, bn=bn, prepacked=False)
+                               side_input_scale=L.side_input_scale, bn=bn, prepacked=False,
+                               activ_alpha=act_alpha, activ_beta=act_beta)
     h = stream.cuda_stream
 
     def step(a=run_args):
@@ -269,7 +284,7 @@ def main():
     value = ops * args.steps / wall / 1e12
     alg_bytes = algorithmic_bytes(L, args.per_channel_scale)
     # The committed counters were taken with the default epilogue.
-    traffic = (None if args.per_channel_scale or args.cudnn7_order
+    traffic = (None if args.per_channel_scale or args.cudnn7_order or args.activation
                else measured_traffic(L.name, plan.kernel_name))
     # Bound: the roofline the layer meets first (ridge = peak ops / peak bytes).
     ridge = PEAK_TOPS[L.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -301,7 +316,8 @@ def main():
                    "kernel": plan.kernel_name},
         "epilogue": ("cuDNN %d order, %s conv_input_scale" %
                      (order, "per-channel" if args.per_channel_scale else "scalar")
-                     if L.dtype == "int8" else "bias, batch norm, ReLU"),
+                     if L.dtype == "int8" else "bias, batch norm, " +
+                     (args.activation or "relu")),
         "launch": "hip graph of the K steps, replayed once",
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TOPS[L.dtype], 3),
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),

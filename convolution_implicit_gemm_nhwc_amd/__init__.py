@@ -19,7 +19,8 @@ __all__ = ["Plan", "FconvError", "DTYPES", "OPS"]
 
 DTYPES = {"int8": _abi.FCONV_INT8, "bf16": _abi.FCONV_BF16, "fp32": _abi.FCONV_FP32}
 OPS = {"scale": _abi.OP_SCALE, "side": _abi.OP_SIDE, "bias": _abi.OP_BIAS,
-       "bn": _abi.OP_BN, "relu": _abi.OP_RELU}
+       "bn": _abi.OP_BN, "relu": _abi.OP_RELU, "leaky_relu": _abi.OP_LEAKY_RELU,
+       "clipped_relu": _abi.OP_CLIPPED_RELU, "clamp": _abi.OP_CLAMP}
 PADDINGS = {"SAME": _abi.FCONV_PAD_SAME, "VALID": _abi.FCONV_PAD_VALID}
 
 
@@ -111,7 +112,8 @@ class Plan:
             "fconv_plan_pack_filter")
 
     def make_args(self, x, w, y, workspace, bias=None, side=None, conv_input_scale=1.0,
-                  side_input_scale=0.0, bn=None, prepacked=False, workspace_bytes=None):
+                  side_input_scale=0.0, bn=None, prepacked=False, workspace_bytes=None,
+                  activ_alpha=0.0, activ_beta=0.0):
         a = _abi.FconvArgs()
         a.x, a.w, a.y = _addr(x), _addr(w), _addr(y)
         a.workspace = _addr(workspace)
@@ -134,6 +136,7 @@ class Plan:
             a.bn_mean, a.bn_var = _addr(bn["mean"]), _addr(bn["var"])
             a.bn_eps = bn["eps"]
         a.flags = _abi.FCONV_RUN_FILTER_PREPACKED if prepacked else 0
+        a.activ_alpha, a.activ_beta = activ_alpha, activ_beta
         return a
 
     def run_args(self, args, stream=None) -> int:

@@ -16,6 +16,7 @@ FCONV_ERR_DEVICE = 5
 FCONV_INT8, FCONV_BF16, FCONV_FP32 = 0, 1, 2
 FCONV_PAD_SAME, FCONV_PAD_VALID = 0, 1
 OP_SCALE, OP_SIDE, OP_BIAS, OP_BN, OP_RELU = 1, 2, 3, 4, 5
+OP_LEAKY_RELU, OP_CLIPPED_RELU, OP_CLAMP = 6, 7, 8
 FCONV_MAX_OPS = 8
 FCONV_RUN_FILTER_PREPACKED = 1
 FCONV_DESC_CUDNN7_ORDER = 1
@@ -41,7 +42,8 @@ class FconvArgs(ctypes.Structure):
                 ("bn_var", ctypes.c_void_p), ("bn_eps", ctypes.c_float),
                 ("y", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32),
-                ("conv_input_scales", ctypes.c_void_p)]
+                ("conv_input_scales", ctypes.c_void_p), ("activ_alpha", ctypes.c_float),
+                ("activ_beta", ctypes.c_float)]
 
 
 class LibraryMissing(RuntimeError):

@@ -121,6 +121,8 @@ struct ConvArgs {
   int32_t use_side, use_bias, use_bn, relu;
   const float* cis_vec;  // per-channel conv_input_scale [K], or null: cis for all
   int32_t cudnn7;        // int8 epilogue in the cuDNN 7 order
+  int32_t act;           // float activation: 0 none, 1 ReLU, 2 leaky, 3 clipped, 4 clamp
+  float act_alpha, act_beta;
   // Row-halo kernel: output rows per workgroup and rows of its first phase
   // (set by its launcher).
   int32_t halo_rows, halo_rows_a;
@@ -295,7 +297,13 @@ __device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArg
     float x = v[e];
     if (a.use_bias) x = x + P.bias[e];
     if (a.use_bn) x = (x - P.mean[e]) * P.sc[e] + P.beta[e];
-    if (a.relu) x = __builtin_fmaxf(x, 0.0f);
+    switch (a.act) {  // uniform
+      case 1: x = __builtin_fmaxf(x, 0.0f); break;
+      case 2: x = x > 0.0f ? x : a.act_alpha * x; break;
+      case 3: x = __builtin_fminf(__builtin_fmaxf(x, 0.0f), a.act_alpha); break;
+      case 4: x = __builtin_fminf(__builtin_fmaxf(x, a.act_alpha), a.act_beta); break;
+      default: break;
+    }
     t[e] = x;
   }
   const int64_t off = static_cast<int64_t>(m) * a.K + ch0;
@@ -1885,6 +1893,9 @@ fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) 
   a.use_bias = p->op_bias;
   a.use_bn = p->op_bn;
   a.relu = p->op_relu;
+  a.act = p->act;
+  a.act_alpha = args->activ_alpha;
+  a.act_beta = args->activ_beta;
   if (fconv::launch_conv(p, a, s) != hipSuccess) return FCONV_ERR_DEVICE;
   return FCONV_OK;
 }

@@ -47,6 +47,7 @@ fconv_status parse_ops(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
   if (d.n_ops < 0 || d.n_ops > FCONV_MAX_OPS) return FCONV_ERR_INVALID_ARG;
   p->op_scale = p->op_side = p->op_bias = p->op_bn = p->op_relu = false;
+  p->act = 0;
   int i = 0;
   auto next_is = [&](int32_t op) {
     if (i < d.n_ops && d.ops[i] == op) {
@@ -64,10 +65,15 @@ fconv_status parse_ops(fconv_plan_s* p) {
     p->op_relu = next_is(FCONV_OP_RELU);
     if (!p->op_scale || !p->op_bias) return FCONV_ERR_UNSUPPORTED;
   } else {
-    // MIOpen supported fusions: conv -> bias -> batch norm -> activation.
+    // MIOpen supported fusions: conv -> bias -> batch norm -> activation
+    // (Relu, Leaky Relu, Clipped Relu or CLAMP).
     p->op_bias = next_is(FCONV_OP_BIAS);
     p->op_bn = next_is(FCONV_OP_BN);
     p->op_relu = next_is(FCONV_OP_RELU);
+    if (p->op_relu) p->act = 1;
+    else if (next_is(FCONV_OP_LEAKY_RELU)) p->act = 2;
+    else if (next_is(FCONV_OP_CLIPPED_RELU)) p->act = 3;
+    else if (next_is(FCONV_OP_CLAMP)) p->act = 4;
   }
   if (i != d.n_ops) return FCONV_ERR_UNSUPPORTED;
   return FCONV_OK;
@@ -202,6 +208,11 @@ fconv_status check_run_args(const fconv_plan_s* p, const fconv_args* a) {
   if (p->op_bn && (!a->bn_gamma || !a->bn_beta || !a->bn_mean || !a->bn_var))
     return FCONV_ERR_INVALID_ARG;
   if (a->conv_input_scales && !p->op_scale) return FCONV_ERR_UNSUPPORTED;
+  if (p->act >= 2) {
+    const float al = a->activ_alpha, be = a->activ_beta;
+    if (!(al - al == 0.0f)) return FCONV_ERR_INVALID_ARG;  // NaN or infinite
+    if (p->act == 4 && !(be - be == 0.0f && al <= be)) return FCONV_ERR_INVALID_ARG;
+  }
   if (!a->workspace || a->workspace_bytes < p->ws_bytes) return FCONV_ERR_WORKSPACE;
   if (!aligned(a->x, 16) || !aligned(a->y, 16) || !aligned(a->workspace, 16) ||
       (!prepacked && !aligned(a->w, 16)) || (p->op_side && !aligned(a->side, 16)))

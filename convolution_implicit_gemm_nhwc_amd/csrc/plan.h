@@ -44,6 +44,7 @@ struct fconv_plan_s {
   int32_t chunk_elems; // elements per 16-byte chunk (16 int8, 8 bf16, 4 fp32)
   bool op_scale, op_side, op_bias, op_bn, op_relu;
   bool cudnn7;          // int8 epilogue in the cuDNN 7 order (FCONV_DESC_CUDNN7_ORDER)
+  int32_t act;          // float activation: 0 none, 1 ReLU, 2 leaky, 3 clipped, 4 clamp
   int64_t M;      // N * Ho * Wo, rows of the implicit GEMM
   int32_t Kg;     // R * S * C, reduction length
   int32_t KgP;    // Kg rounded up to whole k-steps (4 chunks)

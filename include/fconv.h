@@ -35,7 +35,13 @@
  *       t = gamma[k] * (t - mean[k]) / sqrt(var[k] + eps) + beta[k]
  *                                                              FCONV_OP_BN
  *       t = max(t, 0)                                          FCONV_OP_RELU
+ *         or t > 0 ? t : alpha * t                             FCONV_OP_LEAKY_RELU
+ *         or min(max(t, 0), alpha)                             FCONV_OP_CLIPPED_RELU
+ *         or min(max(t, alpha), beta)                          FCONV_OP_CLAMP
  *       y = t (fp32) or bf16(t) rounded to nearest even
+ *   (alpha, beta: fconv_args.activ_alpha / activ_beta.  The fusion tables
+ *   list these activations without formulas; these are their plain
+ *   readings.)
  *
  * Plan / args split (MIOpen "Using the fusion API": a plan holds the data
  * geometry and the ordered operators and is compiled once; the per-run
@@ -91,13 +97,17 @@ typedef enum { FCONV_PAD_SAME = 0, FCONV_PAD_VALID = 1 } fconv_padding;
  * FCONV_ERR_UNSUPPORTED at plan creation, as MIOpen reports unsupported
  * operator sequences when they are added):
  *   FCONV_INT8:       SCALE, [SIDE], BIAS, [RELU]
- *   FCONV_BF16/FP32:  [BIAS], [BN], [RELU]   (each optional, this order) */
+ *   FCONV_BF16/FP32:  [BIAS], [BN], [RELU | LEAKY_RELU | CLIPPED_RELU | CLAMP]
+ *                     (each optional, this order) */
 typedef enum {
   FCONV_OP_SCALE = 1,
   FCONV_OP_SIDE = 2,
   FCONV_OP_BIAS = 3,
   FCONV_OP_BN = 4,
-  FCONV_OP_RELU = 5
+  FCONV_OP_RELU = 5,
+  FCONV_OP_LEAKY_RELU = 6,   /* bf16 / fp32 only */
+  FCONV_OP_CLIPPED_RELU = 7, /* bf16 / fp32 only */
+  FCONV_OP_CLAMP = 8         /* bf16 / fp32 only */
 } fconv_op;
 
 #define FCONV_MAX_OPS 8
@@ -141,6 +151,8 @@ typedef struct fconv_plan_s* fconv_plan;
  *          output channel, which replaces the scalar (TensorFlow
  *          conv_ops_fused_int8.cc slices a scale tensor of more than one
  *          element at the output channel); int8 plans only
+ *   activ_alpha, activ_beta: arguments of the LEAKY_RELU / CLIPPED_RELU /
+ *          CLAMP activation (finite; CLAMP needs alpha <= beta)
  *   bn_gamma, bn_beta, bn_mean, bn_var: device fp32 [K] (needed iff BN op)
  *   bn_eps: batch-norm epsilon
  *   y      device, NHWC [N][Ho][Wo][K] of the plan dtype; must not overlap
@@ -167,6 +179,8 @@ typedef struct {
   size_t workspace_bytes;
   uint32_t flags;
   const float* conv_input_scales;
+  float activ_alpha;
+  float activ_beta;
 } fconv_args;
 
 /* Validates `desc`, resolves output size and padding, checks the operator

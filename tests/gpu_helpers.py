@@ -51,7 +51,7 @@ def make_plan(N, H, W, C, K, R, S, stride, padding, dtype, ops, cudnn7_order=Fal
 
 
 def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
-            prepacked_ws=None, guard=0, dev=None):
+            prepacked_ws=None, guard=0, dev=None, activ=(0.0, 0.0)):
     """Run the plan on device copies of numpy inputs; returns (y, guards_ok)."""
     dev = dev or device()
     tdt = {"int8": torch.int8, "bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
@@ -75,7 +75,8 @@ def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
     # cis: a scalar, or a numpy fp32 vector of one scale per output channel
     cis_arg = to_dev(np.asarray(cis, np.float32), dev) if np.ndim(cis) > 0 else float(cis)
     plan.run(xd, wd, y, ws, bias=bd, side=sd, conv_input_scale=cis_arg,
-             side_input_scale=float(sis), bn=bnd, prepacked=prepacked_ws is not None)
+             side_input_scale=float(sis), bn=bnd, prepacked=prepacked_ws is not None,
+             activ_alpha=float(activ[0]), activ_beta=float(activ[1]))
     torch.cuda.synchronize()
     out = from_dev(y, dtype)
     guards_ok = True

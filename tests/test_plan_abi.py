@@ -78,7 +78,10 @@ def test_create_valid_filter_larger_than_image():
     ([1, 3, 5, 5], 0, False), ([], 0, False), ([1, 2, 2, 3], 0, False),
     ([], 1, True), ([3, 4, 5], 1, True), ([4, 5], 2, True), ([5], 2, True),
     ([3], 2, True), ([4, 3], 1, False), ([1, 3], 2, False), ([2], 1, False),
-    ([5, 3], 2, False), ([9], 1, False)])
+    ([5, 3], 2, False), ([9], 1, False),
+    ([3, 4, 6], 1, True), ([3, 7], 2, True), ([8], 1, True), ([4, 8], 2, True),
+    ([1, 3, 6], 0, False), ([1, 3, 8], 0, False), ([5, 6], 1, False), ([6, 5], 2, False),
+    ([7, 3], 1, False), ([6, 7], 2, False)])
 def test_operator_sequences(ops, dtype, ok):
     st = _create(_desc(ops=ops, dtype=dtype))
     assert st == (_abi.FCONV_OK if ok else _abi.FCONV_ERR_UNSUPPORTED)
@@ -236,3 +239,15 @@ def test_run_checks_per_channel_scales():
     af = pf.make_args(x, w, y, wsp, workspace_bytes=pf.workspace_bytes, bias=kw["bias"])
     af.conv_input_scales = FAKE + 2 ** 25
     assert pf.run_args(af, stream=0) == _abi.FCONV_ERR_UNSUPPORTED
+
+
+def test_run_checks_activation_arguments():
+    x, y, w, wsp, bias = FAKE, FAKE + 2 ** 20, FAKE + 2 ** 22, FAKE + 2 ** 23, FAKE + 2 ** 24
+    for op, alpha, beta, ok in [("clamp", 0.5, 0.25, False), ("clamp", float("nan"), 1.0, False),
+                                ("clamp", -1.0, float("inf"), False),
+                                ("leaky_relu", float("inf"), 0.0, False),
+                                ("clipped_relu", float("nan"), 0.0, False)]:
+        p = fc.Plan(2, 8, 8, 16, 16, 3, 3, 1, "SAME", "fp32", ["bias", op])
+        a = p.make_args(x, w, y, wsp, workspace_bytes=p.workspace_bytes, bias=bias,
+                        activ_alpha=alpha, activ_beta=beta)
+        assert p.run_args(a, stream=0) == _abi.FCONV_ERR_INVALID_ARG, (op, alpha, beta)

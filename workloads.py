@@ -90,6 +90,16 @@ LAYERS = {
         "resnet_3x3_fp32_bn", "fp32", N=16, H=28, W=28, C=256, K=256, R=3, S=3,
         stride=1, padding="SAME", Ho=28, Wo=28, ops=(OP_BIAS, OP_BN, OP_RELU),
         seed=4, description="N=16 28x28x256 -> 256, 3x3 s1 SAME, fp32, bias+BN+ReLU"),
+    # Two more filter sizes of the CBNA "Direct" row of MIOpen's bf16 fusion
+    # table (3x3 .. 11x11, stride 1 and 2), drawn like the 3x3 bf16 layer.
+    "cbna_5x5_bf16": Layer(
+        "cbna_5x5_bf16", "bf16", N=16, H=28, W=28, C=128, K=128, R=5, S=5,
+        stride=1, padding="SAME", Ho=28, Wo=28, ops=(OP_BIAS, OP_BN, OP_RELU),
+        seed=5, description="N=16 28x28x128 -> 128, 5x5 s1 SAME, bf16, bias+BN+ReLU"),
+    "cbna_7x7s2_bf16": Layer(
+        "cbna_7x7s2_bf16", "bf16", N=16, H=56, W=56, C=64, K=128, R=7, S=7,
+        stride=2, padding="SAME", Ho=28, Wo=28, ops=(OP_BIAS, OP_BN, OP_RELU),
+        seed=6, description="N=16 56x56x64 -> 128, 7x7 s2 SAME (pads 2/3), bf16, bias+BN+ReLU"),
 }
 
 
