@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--activation", default=None, metavar="NAME[:ALPHA[:BETA]]",
                     help="bf16/fp32: replace the layer's ReLU by leaky_relu, clipped_relu or "
                          "clamp with these arguments")
+    ap.add_argument("--autotune", action="store_true",
+                    help="time every kernel configuration for the layer first and run the "
+                         "fastest (fconv_plan_autotune)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="instead of the conv, time a plain device-to-device copy of "
                          "BYTES bytes (the reference kernel for counter calibration)")
@@ -210,6 +213,12 @@ def main():
                                side_input_scale=L.side_input_scale, bn=bn, prepacked=False,
                                activ_alpha=act_alpha, activ_beta=act_beta)
     h = stream.cuda_stream
+    heuristic_kernel = plan.kernel_name
+    if args.autotune:
+        fc.autotune_cache_clear()
+        plan.autotune(x, w, y, ws, repeats=20, stream=stream, bias=bias, side=side,
+                      conv_input_scale=cis, side_input_scale=L.side_input_scale, bn=bn,
+                      prepacked=True, activ_alpha=act_alpha, activ_beta=act_beta)
 
     def step(a=run_args):
         st = plan.run_args(a, h)
@@ -285,7 +294,7 @@ def main():
     alg_bytes = algorithmic_bytes(L, args.per_channel_scale)
     # The committed counters were taken with the default epilogue.
     traffic = (None if args.per_channel_scale or args.cudnn7_order or args.activation
-               else measured_traffic(L.name, plan.kernel_name))
+               or args.autotune else measured_traffic(L.name, plan.kernel_name))
     # Bound: the roofline the layer meets first (ridge = peak ops / peak bytes).
     ridge = PEAK_TOPS[L.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ops / alg_bytes <= ridge:
@@ -313,7 +322,9 @@ def main():
         "config": {"workload": L.name, "layer": L.description, "N": L.N, "H": L.H, "W": L.W,
                    "C": L.C, "K": L.K, "R": L.R, "S": L.S, "stride": L.stride,
                    "padding": L.padding, "filter": "prepacked once per plan",
-                   "kernel": plan.kernel_name},
+                   "kernel": plan.kernel_name,
+                   "kernel_choice": "autotuned (heuristic: %s)" % heuristic_kernel
+                   if args.autotune else "heuristic"},
         "epilogue": ("cuDNN %d order, %s conv_input_scale" %
                      (order, "per-channel" if args.per_channel_scale else "scalar")
                      if L.dtype == "int8" else "bias, batch norm, " +

@@ -143,6 +143,19 @@ class Plan:
         """Enqueue with a prepared FconvArgs; returns the raw status."""
         return _abi.lib().fconv_plan_run(self._h, _stream_handle(stream), ctypes.byref(args))
 
+    def autotune(self, x, w, y, workspace, repeats=20, stream=None, **kw):
+        """Time every kernel configuration for this shape on these buffers and
+        keep the fastest (see fconv_plan_autotune); returns its microseconds
+        per launch.  y holds the chosen configuration's result."""
+        best = ctypes.c_float()
+        _check(_abi.lib().fconv_plan_autotune(self._h, _stream_handle(stream),
+                                              ctypes.byref(self.make_args(x, w, y, workspace,
+                                                                          **kw)),
+                                              int(repeats), ctypes.byref(best)),
+               "fconv_plan_autotune")
+        self.kernel_name = _abi.lib().fconv_plan_kernel_name(self._h).decode()
+        return best.value
+
     def run(self, x, w, y, workspace, stream=None, **kw):
         _check(self.run_args(self.make_args(x, w, y, workspace, **kw), stream),
                "fconv_plan_run")
@@ -155,3 +168,8 @@ class Plan:
         y = torch.empty(self.out_shape, dtype=tdt, device=x.device)
         ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=x.device)
         return self.run(x, w, y, ws, stream=stream, **kw)
+
+
+def autotune_cache_clear():
+    """Forget every autotuned configuration of this process."""
+    _abi.lib().fconv_autotune_cache_clear()

@@ -24,7 +24,8 @@ FCONV_DESC_CUDNN7_ORDER = 1
 # Every symbol include/fconv.h declares.
 EXPORTS = ("fconv_plan_create", "fconv_plan_output_dims", "fconv_plan_workspace_size",
            "fconv_plan_pack_filter", "fconv_plan_run", "fconv_plan_destroy",
-           "fconv_plan_kernel_name", "fconv_status_string")
+           "fconv_plan_kernel_name", "fconv_status_string", "fconv_plan_autotune",
+           "fconv_autotune_cache_clear")
 
 
 class FconvDesc(ctypes.Structure):
@@ -81,6 +82,11 @@ def lib():
         L.fconv_plan_destroy.restype = st
         L.fconv_plan_kernel_name.argtypes = [P]
         L.fconv_plan_kernel_name.restype = ctypes.c_char_p
+        L.fconv_plan_autotune.argtypes = [P, P, ctypes.POINTER(FconvArgs), ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_float)]
+        L.fconv_plan_autotune.restype = st
+        L.fconv_autotune_cache_clear.argtypes = []
+        L.fconv_autotune_cache_clear.restype = None
         L.fconv_status_string.argtypes = [st]
         L.fconv_status_string.restype = ctypes.c_char_p
         _lib = L

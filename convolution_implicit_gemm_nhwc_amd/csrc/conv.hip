@@ -35,7 +35,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <math.h>
+#include <string.h>
+
 #include <algorithm>
+#include <vector>
 
 #include "plan.h"
 
@@ -1840,26 +1844,12 @@ hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
 }  // namespace
 }  // namespace fconv
 
-extern "C" {
+namespace fconv {
+namespace {
 
-fconv_status fconv_plan_pack_filter(fconv_plan p, void* stream, const void* w,
-                                    void* workspace, size_t workspace_bytes) {
-  fconv_status st = fconv::check_pack_args(p, w, workspace, workspace_bytes);
-  if (st != FCONV_OK) return st;
-  hipError_t e = fconv::launch_pack_any(p, w, workspace, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FCONV_OK : FCONV_ERR_DEVICE;
-}
-
-fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) {
-  fconv_status st = fconv::check_run_args(p, args);
-  if (st != FCONV_OK) return st;
-  if (p->M == 0) return FCONV_OK;  // empty batch: nothing to compute
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!(args->flags & FCONV_RUN_FILTER_PREPACKED)) {
-    if (fconv::launch_pack_any(p, args->w, args->workspace, s) != hipSuccess)
-      return FCONV_ERR_DEVICE;
-  }
-  fconv::ConvArgs a;
+// Kernel arguments of one run of the plan.
+ConvArgs make_conv_args(const fconv_plan_s* p, const fconv_args* args) {
+  ConvArgs a;
   a.x = args->x;
   a.wp = args->workspace;
   a.bias = args->bias;
@@ -1896,7 +1886,124 @@ fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) 
   a.act = p->act;
   a.act_alpha = args->activ_alpha;
   a.act_beta = args->activ_beta;
+  return a;
+}
+
+// Normwise difference of two outputs of the plan, max|a - b| / max|a|
+// (int8: 0 if bit-identical, else 1).
+double output_difference(const fconv_plan_s* p, const std::vector<uint8_t>& a,
+                         const std::vector<uint8_t>& b) {
+  if (p->d.dtype == FCONV_INT8) return memcmp(a.data(), b.data(), a.size()) == 0 ? 0.0 : 1.0;
+  double num = 0.0, den = 0.0;
+  const size_t n = static_cast<size_t>(p->y_elems);
+  for (size_t i = 0; i < n; ++i) {
+    float x, y;
+    if (p->d.dtype == FCONV_BF16) {
+      uint32_t ux = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(a.data())[i]) << 16;
+      uint32_t uy = static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(b.data())[i]) << 16;
+      memcpy(&x, &ux, 4);
+      memcpy(&y, &uy, 4);
+    } else {
+      x = reinterpret_cast<const float*>(a.data())[i];
+      y = reinterpret_cast<const float*>(b.data())[i];
+    }
+    num = std::max(num, static_cast<double>(std::fabs(x - y)));
+    den = std::max(den, static_cast<double>(std::fabs(x)));
+  }
+  return den > 0.0 ? num / den : num;
+}
+
+}  // namespace
+}  // namespace fconv
+
+extern "C" {
+
+fconv_status fconv_plan_pack_filter(fconv_plan p, void* stream, const void* w,
+                                    void* workspace, size_t workspace_bytes) {
+  fconv_status st = fconv::check_pack_args(p, w, workspace, workspace_bytes);
+  if (st != FCONV_OK) return st;
+  hipError_t e = fconv::launch_pack_any(p, w, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FCONV_OK : FCONV_ERR_DEVICE;
+}
+
+fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) {
+  fconv_status st = fconv::check_run_args(p, args);
+  if (st != FCONV_OK) return st;
+  if (p->M == 0) return FCONV_OK;  // empty batch: nothing to compute
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(args->flags & FCONV_RUN_FILTER_PREPACKED)) {
+    if (fconv::launch_pack_any(p, args->w, args->workspace, s) != hipSuccess)
+      return FCONV_ERR_DEVICE;
+  }
+  fconv::ConvArgs a = fconv::make_conv_args(p, args);
   if (fconv::launch_conv(p, a, s) != hipSuccess) return FCONV_ERR_DEVICE;
+  return FCONV_OK;
+}
+
+
+fconv_status fconv_plan_autotune(fconv_plan p, void* stream, const fconv_args* args,
+                                 int32_t repeats, float* best_us) {
+  fconv_status st = fconv::check_run_args(p, args);
+  if (st != FCONV_OK) return st;
+  if (repeats < 1 || repeats > 100000) return FCONV_ERR_INVALID_ARG;
+  if (p->M == 0) return FCONV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!(args->flags & FCONV_RUN_FILTER_PREPACKED) &&
+      fconv::launch_pack_any(p, args->w, args->workspace, s) != hipSuccess)
+    return FCONV_ERR_DEVICE;
+  const fconv::ConvArgs a = fconv::make_conv_args(p, args);
+  fconv::KernelConfig cand[16];
+  const int n = fconv::list_configs(p, cand, 16);
+  const size_t ybytes = static_cast<size_t>(p->y_elems) * p->esize;
+  std::vector<uint8_t> ref(ybytes), out(ybytes);
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return FCONV_ERR_DEVICE;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return FCONV_ERR_DEVICE;
+  }
+  // Agreement with the plan's own configuration (the first candidate):
+  // bit-exact for int8, the float tolerances otherwise.
+  const double tol = p->d.dtype == FCONV_INT8 ? 0.0 : p->d.dtype == FCONV_BF16 ? 2e-2 : 1e-5;
+  float best = -1.0f;
+  int best_i = 0;
+  st = FCONV_OK;
+  for (int i = 0; i < n && st == FCONV_OK; ++i) {
+    fconv_plan_s q = *p;
+    fconv::apply_config(&q, cand[i]);
+    if (fconv::launch_conv(&q, a, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+      if (i == 0) st = FCONV_ERR_DEVICE;
+      (void)hipGetLastError();
+      continue;
+    }
+    if (hipMemcpy((i == 0 ? ref : out).data(), args->y, ybytes, hipMemcpyDeviceToHost) !=
+        hipSuccess) {
+      st = FCONV_ERR_DEVICE;
+      break;
+    }
+    if (i > 0 && fconv::output_difference(p, ref, out) > tol) continue;
+    bool ok = hipEventRecord(e0, s) == hipSuccess;
+    for (int r = 0; ok && r < repeats; ++r) ok = fconv::launch_conv(&q, a, s) == hipSuccess;
+    ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.0f;
+    if (!ok || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      st = FCONV_ERR_DEVICE;
+      break;
+    }
+    if (best < 0.0f || ms < best) {
+      best = ms;
+      best_i = i;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != FCONV_OK) return st;
+  fconv::apply_config(p, cand[best_i]);
+  fconv::cache_store(p->d, cand[best_i]);
+  if (best_us) *best_us = best * 1000.0f / static_cast<float>(repeats);
+  // Leave y holding the chosen configuration's result.
+  if (fconv::launch_conv(p, a, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return FCONV_ERR_DEVICE;
   return FCONV_OK;
 }
 

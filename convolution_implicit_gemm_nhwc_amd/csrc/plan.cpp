@@ -11,7 +11,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <new>
+#include <string>
 
 #include "plan.h"
 
@@ -163,6 +166,62 @@ void choose_variant(fconv_plan_s* p) {
   p->kernel_name = kernel_name(p->variant, d.dtype);
 }
 
+// Shape conditions of each family, as choose_variant applies them.
+struct FamilyFit {
+  bool rf, tile, stream, halo;
+};
+
+FamilyFit family_fit(const fconv_plan_s* p) {
+  const fconv_desc& d = p->d;
+  const int64_t rf_lds = 64 * static_cast<int64_t>(p->wrow_bytes);
+  const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
+  const bool sizes_ok = x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31) &&
+                        static_cast<int64_t>(p->ws_bytes) < (int64_t{1} << 31);
+  FamilyFit f;
+  const bool tap = p->load_mode == kLoadTap && d.K % 16 == 0 && sizes_ok;
+  f.tile = tap && (static_cast<int64_t>(d.C) * p->esize) % 128 == 0;
+  f.rf = tap && rf_lds <= kRfMaxLds;
+  const int32_t cs = d.C / 64;
+  const bool shape_ok = (d.R == 3 && d.S == 3 && cs == 1) ||
+                        (d.R == 1 && d.S == 1 && (cs == 1 || cs == 2 || cs == 4 || cs == 8));
+  const int64_t tiles = (p->M + 15) / 16;
+  f.stream = f.rf && d.dtype == FCONV_INT8 && shape_ok && tiles * 1024 < (int64_t{1} << 31);
+  f.halo = f.stream && d.R == 3 && d.S == 3 && cs == 1 && d.stride_h == 1 && d.stride_w == 1 &&
+           d.W + p->pl + p->pr <= 64;
+  return f;
+}
+
+fconv_desc cache_key(const fconv_desc& d) {
+  fconv_desc k;
+  memset(&k, 0, sizeof(k));
+  k = d;
+  for (int i = d.n_ops < 0 ? 0 : d.n_ops; i < FCONV_MAX_OPS; ++i) k.ops[i] = 0;
+  return k;
+}
+
+std::mutex& cache_mutex() {
+  static std::mutex m;
+  return m;
+}
+
+std::map<std::string, KernelConfig>& cache_map() {
+  static std::map<std::string, KernelConfig> m;
+  return m;
+}
+
+std::string key_bytes(const fconv_desc& d) {
+  const fconv_desc k = cache_key(d);
+  return std::string(reinterpret_cast<const char*>(&k), sizeof(k));
+}
+
+bool cache_lookup(const fconv_desc& d, KernelConfig* c) {
+  std::lock_guard<std::mutex> lock(cache_mutex());
+  auto it = cache_map().find(key_bytes(d));
+  if (it == cache_map().end()) return false;
+  *c = it->second;
+  return true;
+}
+
 bool aligned(const void* ptr, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
 }
@@ -176,6 +235,41 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace
 
 namespace fconv {
+
+int list_configs(const fconv_plan_s* p, KernelConfig* out, int max) {
+  int n = 0;
+  auto add = [&](int32_t v, int32_t pt, int32_t rd, int32_t hr) {
+    for (int i = 0; i < n; ++i)
+      if (out[i].variant == v && out[i].pixel_tiles == pt && out[i].ring_depth == rd &&
+          out[i].halo_rows == hr)
+        return;
+    if (n < max) out[n++] = KernelConfig{v, pt, rd, hr};
+  };
+  add(p->variant, p->pixel_tiles, p->ring_depth, p->halo_rows);
+  const FamilyFit f = family_fit(p);
+  if (f.halo) add(kHalo, 1, 0, 0);
+  if (f.stream) add(kStream, 1, 0, 0);
+  if (f.tile) add(kTiled, 1, 0, 0);
+  if (f.rf) {
+    static const int32_t pt_rd[6][2] = {{1, 4}, {1, 9}, {2, 4}, {2, 9}, {4, 2}, {4, 4}};
+    for (const auto& c : pt_rd) add(kResidentFilter, c[0], c[1], 0);
+  }
+  add(kGeneral, 1, 0, 0);
+  return n;
+}
+
+void apply_config(fconv_plan_s* p, const KernelConfig& c) {
+  p->variant = c.variant;
+  p->pixel_tiles = c.pixel_tiles;
+  p->ring_depth = c.ring_depth;
+  p->halo_rows = c.halo_rows;
+  p->kernel_name = kernel_name(c.variant, p->d.dtype);
+}
+
+void cache_store(const fconv_desc& d, const KernelConfig& c) {
+  std::lock_guard<std::mutex> lock(cache_mutex());
+  cache_map()[key_bytes(d)] = c;
+}
 
 // s = ceil(log2 d), m = floor(2^(32+s) / d) + 1 (< 2^33).  For n < 2^31,
 // n*m / 2^(32+s) exceeds n/d by less than 2^-(s+1) <= 1/(2d), which never
@@ -302,6 +396,10 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
   p->ho_div = make_fast_div(static_cast<uint32_t>(p->Ho));
   choose_variant(p);
+  // A configuration autotuned earlier in this process for the same
+  // descriptor wins, unless a family is pinned through the environment.
+  KernelConfig cached;
+  if (!getenv("FCONV_FORCE_VARIANT") && cache_lookup(p->d, &cached)) apply_config(p, cached);
   *out = p;
   return FCONV_OK;
 }
@@ -332,6 +430,11 @@ fconv_status fconv_plan_destroy(fconv_plan p) {
 }
 
 const char* fconv_plan_kernel_name(fconv_plan p) { return p ? p->kernel_name : nullptr; }
+
+void fconv_autotune_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(cache_mutex());
+  cache_map().clear();
+}
 
 const char* fconv_status_string(fconv_status s) {
   switch (s) {

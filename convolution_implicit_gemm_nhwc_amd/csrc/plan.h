@@ -62,6 +62,19 @@ struct fconv_plan_s {
 };
 
 namespace fconv {
+// One kernel configuration of a plan: the family and its tiling knobs.
+struct KernelConfig {
+  int32_t variant, pixel_tiles, ring_depth, halo_rows;
+};
+// The configurations that can run the plan's shape, the plan's current one
+// first; returns how many were written (at most max).
+int list_configs(const fconv_plan_s* p, KernelConfig* out, int max);
+// Make `c` the plan's configuration (and kernel name).
+void apply_config(fconv_plan_s* p, const KernelConfig& c);
+// Process-wide cache of autotuned configurations, keyed by the plan
+// descriptor (the operator list past n_ops ignored).
+void cache_store(const fconv_desc& d, const KernelConfig& c);
+
 // Argument checks of fconv_plan_run / fconv_plan_pack_filter that need no
 // device: pointers, alignment, workspace size, aliasing.  Implemented in
 // plan.cpp.

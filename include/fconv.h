@@ -220,6 +220,27 @@ FCONV_API fconv_status fconv_plan_pack_filter(fconv_plan plan, void* stream, con
  * FCONV_ERR_DEVICE (launch failure). */
 FCONV_API fconv_status fconv_plan_run(fconv_plan plan, void* stream, const fconv_args* args);
 
+/* Autotuning, as TensorFlow (conv_ops_fused_int8.cc, the autotune path of
+ * LaunchFusedConv2DOpGpuInt8Helper) and MXNet (cudnn_deconvolution-inl.h,
+ * SelectAlgo) pick among algorithms by timing them and caching the choice per
+ * problem key.  Times every kernel configuration that can run the plan's
+ * shape (family and tiling), `repeats` launches each, on the caller's
+ * buffers `args` (checked as by fconv_plan_run; y is overwritten and holds
+ * the chosen configuration's result on return).  A candidate whose output
+ * differs from the plan's own configuration (int8: any bit; bf16: normwise
+ * 2e-2; fp32: 1e-5) is not chosen.  The fastest becomes the plan's
+ * configuration and is cached for the process: later fconv_plan_create calls
+ * with the same descriptor start from it (unless FCONV_FORCE_VARIANT pins a
+ * family).  Synchronous: returns after the stream has drained.  Must not
+ * run concurrently with other calls on the same plan.  *best_us (may be
+ * NULL) receives the chosen configuration's time per launch.  Errors: as
+ * fconv_plan_run; FCONV_ERR_INVALID_ARG for repeats outside 1..100000. */
+FCONV_API fconv_status fconv_plan_autotune(fconv_plan plan, void* stream, const fconv_args* args,
+                                           int32_t repeats, float* best_us);
+
+/* Forget every autotuned configuration of this process. */
+FCONV_API void fconv_autotune_cache_clear(void);
+
 /* Frees the plan (host memory only).  NULL is a no-op. */
 FCONV_API fconv_status fconv_plan_destroy(fconv_plan plan);
 

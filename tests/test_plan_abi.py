@@ -251,3 +251,17 @@ def test_run_checks_activation_arguments():
         a = p.make_args(x, w, y, wsp, workspace_bytes=p.workspace_bytes, bias=bias,
                         activ_alpha=alpha, activ_beta=beta)
         assert p.run_args(a, stream=0) == _abi.FCONV_ERR_INVALID_ARG, (op, alpha, beta)
+
+
+def test_autotune_checks_its_arguments():
+    p, (x, w, y, wsp), kw, ws = _plan_and_args()
+    L = _abi.lib()
+    a = p.make_args(x, w, y, wsp, workspace_bytes=ws, **kw)
+    assert L.fconv_plan_autotune(p.handle, None, ctypes.byref(a), 0, None) == \
+        _abi.FCONV_ERR_INVALID_ARG
+    assert L.fconv_plan_autotune(None, None, ctypes.byref(a), 5, None) == \
+        _abi.FCONV_ERR_INVALID_ARG
+    b = p.make_args(None, w, y, wsp, workspace_bytes=ws, **kw)
+    assert L.fconv_plan_autotune(p.handle, None, ctypes.byref(b), 5, None) == \
+        _abi.FCONV_ERR_INVALID_ARG
+    fc.autotune_cache_clear()
