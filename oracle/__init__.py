@@ -72,6 +72,8 @@ def _load():
                                                  ctypes.c_float, i, ctypes.c_float,
                                                  ctypes.c_float, p]
         lib.oracle_epilogue_float_ex.restype = None
+        lib.oracle_wgrad_direct.argtypes = [p, p, p, p]
+        lib.oracle_wgrad_direct.restype = i
         lib.oracle_num_threads.restype = i
         _lib = lib
     return _lib
@@ -150,6 +152,33 @@ def conv_acc(x, w, stride=1, padding="SAME", form="direct"):
     if rc != 0:
         raise OracleError("conv failed (rc=%d)" % rc)
     return acc
+
+
+def _as_f64(a):
+    """float64 copy of float32 data or of bf16 given as uint16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def wgrad(x, dy, R, S, stride=1, padding="SAME"):
+    """Filter gradient dW [R][S][C][K] (float64) of the convolution with
+    input x (NHWC) and output gradient dy (N, Ho, Wo, K); x and dy float32 or
+    bf16 bit patterns (uint16)."""
+    x64 = _as_f64(x)
+    dy64 = _as_f64(dy)
+    K = dy64.shape[-1]
+    w_shape = (R, S, x64.shape[-1], K)
+    stride, pads = resolve(x64.shape, w_shape, stride, padding)
+    d, oshape = _shape_block(x64, np.empty(w_shape), stride, pads)
+    if tuple(dy64.shape) != oshape:
+        raise OracleError("dy shape %s != output shape %s" % (dy64.shape, oshape))
+    dw = np.empty(w_shape, dtype=np.float64)
+    rc = _load().oracle_wgrad_direct(_ptr(x64), _ptr(dy64), _ptr(d), _ptr(dw))
+    if rc != 0:
+        raise OracleError("wgrad failed (rc=%d)" % rc)
+    return dw
 
 
 def epilogue_i8(acc, conv_input_scale, bias, side=None, side_input_scale=0.0,

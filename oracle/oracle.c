@@ -51,6 +51,13 @@
  *    writes both orders' side step alike, and the cuDNN 8 code spells it that
  *    way), with no separate bias step.
  *
+ *  - The weight gradient.  TensorFlow conv_grad_filter_ops.cc,
+ *    Conv2DCustomBackpropFilterOp: per image, the Im2col patch matrix A
+ *    ([Ho*Wo, R*S*C]) and the output gradient B ([Ho*Wo, K]); the filter
+ *    gradient [R*S*C, K] (HWIO) is the sum over images of A^T B.  Written out
+ *    here as the plain sum dW[r,s,c,k] = sum over n, ho, wo of
+ *    X(n, ho*sh - pt + r, wo*sw - pl + s, c) * dY[n,ho,wo,k], in double.
+ *
  *  - The float epilogue.  MIOpen "Using the fusion API": operators apply in
  *    the order they are added, and the supported-fusion tables list
  *    conv -> bias -> batch-norm inference -> activation (CBNA).  Batch-norm
@@ -366,6 +373,38 @@ void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scal
  * in that order, in double.  bias == NULL skips the bias; gamma == NULL skips
  * the batch norm (then beta/mean/var are ignored).
  */
+/*
+ * Weight gradient, in double: x [N][H][W][C], dy [N][Ho][Wo][K] (both as
+ * double), dw [R][S][C][K].  d as for the convolutions.
+ */
+int oracle_wgrad_direct(const double* x, const double* dy, const int* d, double* dw) {
+  shape_t s;
+  if (unpack_shape(d, &s) != ORACLE_OK) return ORACLE_BAD_ARG;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (long r = 0; r < s.R; ++r) {
+    for (long q = 0; q < s.S; ++q) {
+      for (long c = 0; c < s.C; ++c) {
+        double* out = dw + ((r * s.S + q) * s.C + c) * s.K;
+        for (long k = 0; k < s.K; ++k) out[k] = 0.0;
+        for (long n = 0; n < s.N; ++n) {
+          for (long ho = 0; ho < s.Ho; ++ho) {
+            long hi = ho * s.sh - s.pt + r;
+            if (hi < 0 || hi >= s.H) continue;
+            for (long wo = 0; wo < s.Wo; ++wo) {
+              long wi = wo * s.sw - s.pl + q;
+              if (wi < 0 || wi >= s.W) continue;
+              const double xv = x[((n * s.H + hi) * s.W + wi) * s.C + c];
+              const double* g = dy + ((n * s.Ho + ho) * s.Wo + wo) * s.K;
+              for (long k = 0; k < s.K; ++k) out[k] += xv * g[k];
+            }
+          }
+        }
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Activation modes of the float epilogue. */
 #define ORACLE_ACT_NONE 0
 #define ORACLE_ACT_RELU 1

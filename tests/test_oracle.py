@@ -521,3 +521,53 @@ def test_workload_inputs_are_seeded_and_in_range():
             assert a.x.min() >= L.x_range[0] and a.x.max() <= L.x_range[1]
             if L.has_side:
                 assert a.side.shape == (1, L.Ho, L.Wo, L.K)
+
+
+# ------------------------------------------------------ weight gradient
+
+
+def _torch_wgrad(x64, dy64, R, S, stride, pads):
+    """torch's conv2d_weight in float64 (NCHW); asymmetric pads by F.pad."""
+    pt, pb, pl, pr = pads
+    xt = F.pad(torch.from_numpy(x64).permute(0, 3, 1, 2), (pl, pr, pt, pb))
+    gt = torch.from_numpy(dy64).permute(0, 3, 1, 2)
+    g = torch.nn.grad.conv2d_weight(xt, (dy64.shape[-1], x64.shape[-1], R, S), gt,
+                                    stride=stride, padding=0)
+    return g.permute(2, 3, 1, 0).numpy()  # KCRS -> RSCK
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_wgrad_against_torch(seed):
+    """The filter gradient equals torch.nn.grad.conv2d_weight (float64) on
+    random shapes: strides 1-3, SAME (odd pads after) and VALID, filters
+    larger than the image, float32 and bf16 inputs."""
+    rng = np.random.default_rng(100 + seed)
+    N, H, W = int(rng.integers(1, 3)), int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    C, K = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+    R, S = int(rng.choice([1, 2, 3, 5])), int(rng.choice([1, 3, 4]))
+    st = int(rng.integers(1, 4))
+    same = seed % 3 != 0 or H < R or W < S
+    g = oracle.geometry(H, W, R, S, st, st, same)
+    x = rng.standard_normal((N, H, W, C)).astype(np.float32)
+    dy = rng.standard_normal((N, g[0], g[1], K)).astype(np.float32)
+    if seed % 2:
+        x, dy = wl.float_to_bf16_bits(x), wl.float_to_bf16_bits(dy)
+    dw = oracle.wgrad(x, dy, R, S, st, "SAME" if same else "VALID")
+    ref = _torch_wgrad(oracle._as_f64(x), oracle._as_f64(dy), R, S, st, g[2:])
+    np.testing.assert_allclose(dw, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_wgrad_of_a_delta_gradient_is_the_patch():
+    """dY = 1 at one output position and channel, 0 elsewhere: dW[:, :, :, k]
+    is the input patch under that position (zeros in the padding)."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((1, 6, 7, 3)).astype(np.float32)
+    Ho, Wo, pt, pb, pl, pr = oracle.geometry(6, 7, 3, 3, 2, 2, True)
+    for (ho, wo, k) in [(0, 0, 1), (Ho - 1, Wo - 1, 0), (1, 2, 2)]:
+        dy = np.zeros((1, Ho, Wo, 3), np.float32)
+        dy[0, ho, wo, k] = 1.0
+        dw = oracle.wgrad(x, dy, 3, 3, 2, "SAME")
+        xp = np.pad(x[0].astype(np.float64), ((pt, pb), (pl, pr), (0, 0)))
+        patch = xp[2 * ho:2 * ho + 3, 2 * wo:2 * wo + 3, :]
+        np.testing.assert_array_equal(dw[:, :, :, k], patch)
+        assert not np.any(np.delete(dw, k, axis=3))
