@@ -117,6 +117,147 @@ def copy_probe(nbytes: int, steps: int, warmup: int):
           flush=True)
 
 
+def wgrad_cpu_baseline(L, inp, seconds: float):
+    """The oracle's weight gradient on a prefix of the batch (one image, then
+    more while the budget lasts), as FLOP/s of the same formula."""
+    import oracle
+    n_img = 1
+    reps, flops, t0 = 0, 0, time.perf_counter()
+    ref = None
+    while True:
+        ref = oracle.wgrad(inp.x[:n_img], inp.dy[:n_img], L.R, L.S, L.stride, L.padding)
+        reps += 1
+        flops += L.ops_count() // L.N * n_img
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    # The oracle's parallel loop runs over the R*S filter taps.
+    return ref, n_img, dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s",
+                            cores=min(oracle.num_threads(), L.R * L.S), kind="oracle",
+                            sample="first image of the %s batch, %d repetition(s) in %.1f s: "
+                                   "direct loops in double, OpenMP over (r, s)"
+                                   % (L.name, reps, dt))
+
+
+def bench_wgrad(args):
+    """Weight gradient: dw of the layer from x and dy, fp32 dW (bf16 inputs)."""
+    import numpy as np
+    import torch
+
+    import convolution_implicit_gemm_nhwc_amd as fc
+    import workloads as wl
+
+    L = wl.WGRAD_LAYERS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = wl.make_wgrad_inputs(L)
+    plan = fc.WgradPlan(L.N, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
+                        out_fp32=True)
+
+    def put(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, dy = put(inp.x), put(inp.dy)
+    dw = torch.empty(plan.dw_shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(h):
+        st = plan.run_raw(x, dy, dw, ws, stream=h)
+        if st != 0:
+            raise fc.FconvError(st, "fconv_wgrad_plan_run")
+
+    for _ in range(args.warmup):
+        step(stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - t0
+    eager_ms = ev0.elapsed_time(ev1) / args.steps
+
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        with torch.cuda.graph(graph, stream=gstream):
+            for _ in range(args.steps):
+                step(gstream.cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(gstream)
+    with torch.cuda.stream(gstream):
+        graph.replay()
+    g1.record(gstream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = g0.elapsed_time(g1) / args.steps
+    dw_gpu = dw.cpu().numpy()
+
+    ops = L.ops_count()
+    esize = 2 if L.dtype == "bf16" else 4
+    alg_bytes = (L.N * L.H * L.W * L.C + L.N * L.Ho * L.Wo * L.K) * esize + \
+        L.R * L.S * L.C * L.K * 4
+    value = ops * args.steps / wall / 1e12
+    peak = PEAK_TOPS[L.dtype]
+    achieved = ops / (step_ms * 1e-3) / 1e12
+    kernels = plan.kernel_name + ("+wgrad_reduce" if plan.workspace_bytes else "")
+    out = {
+        "metric": "conv weight-gradient TFLOP/s (2*N*Ho*Wo*K*R*S*C/t), 1 GPU",
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16 (fp32 accumulate, fp32 dW)", "fp32": "fp32"}[L.dtype],
+        "data": "synthetic",
+        "config": {"workload": L.name, "layer": L.description, "N": L.N, "H": L.H, "W": L.W,
+                   "C": L.C, "K": L.K, "R": L.R, "S": L.S, "stride": L.stride,
+                   "padding": L.padding, "kernel": kernels,
+                   "pixel_ranges": plan.workspace_bytes // (16 * ((L.R * L.S * L.C * L.K + 3)
+                                                                 // 4)) or 1},
+        "launch": "hip graph of the K steps, replayed once",
+        "pct_of_mfma_peak": round(100.0 * value / peak, 3),
+        "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
+                  "event_us_per_step": round(eager_ms * 1e3, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": kernels, "kernel_avg_us": round(step_ms * 1e3, 3),
+                     "note": "one step = the main kernel and the fixed-order sum of its "
+                             "pixel ranges, timed together",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        ref, n_img, cb = wgrad_cpu_baseline(L, inp, args.cpu_seconds)
+        # The sample's own check: the GPU on the same image prefix.
+        g = fc.WgradPlan(n_img, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
+                         out_fp32=True)
+        dw1 = g(x[:n_img].contiguous(), dy[:n_img].contiguous())
+        torch.cuda.synchronize()
+        got = dw1.cpu().numpy().astype(np.float64)
+        cb["sample_normwise_error_vs_gpu"] = float(np.max(np.abs(got - ref)) /
+                                                   max(np.max(np.abs(ref)), 1e-300))
+        out["cpu_baseline"] = cb
+    else:
+        out["cpu_baseline"] = None
+    del dw_gpu
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +299,9 @@ def main():
     import convolution_implicit_gemm_nhwc_amd as fc
     import workloads as wl
 
+    if args.workload in wl.WGRAD_LAYERS:
+        bench_wgrad(args)
+        return
     L = wl.LAYERS[args.workload]
     if (args.per_channel_scale or args.cudnn7_order) and L.dtype != "int8":
         print("--per-channel-scale and --cudnn7-order apply to int8 layers", file=sys.stderr)

@@ -8,6 +8,9 @@ provides device memory and streams) or raw device addresses given as ints.
     plan = Plan(N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="int8",
                 ops=("scale", "side", "bias", "relu"))
     y = plan(x, w, bias=b, side=s, conv_input_scale=2**-11, side_input_scale=0.25)
+
+    g = WgradPlan(N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="bf16")
+    dw = g(x, dy)          # filter gradient, HWIO
 """
 from __future__ import annotations
 
@@ -15,7 +18,7 @@ import ctypes
 
 from . import _abi
 
-__all__ = ["Plan", "FconvError", "DTYPES", "OPS"]
+__all__ = ["Plan", "WgradPlan", "FconvError", "DTYPES", "OPS"]
 
 DTYPES = {"int8": _abi.FCONV_INT8, "bf16": _abi.FCONV_BF16, "fp32": _abi.FCONV_FP32}
 OPS = {"scale": _abi.OP_SCALE, "side": _abi.OP_SIDE, "bias": _abi.OP_BIAS,
@@ -168,6 +171,71 @@ class Plan:
         y = torch.empty(self.out_shape, dtype=tdt, device=x.device)
         ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=x.device)
         return self.run(x, w, y, ws, stream=stream, **kw)
+
+
+class WgradPlan:
+    """Weight gradient of the convolution with this geometry (see
+    fconv_wgrad_plan_create): dw[r,s,c,k] = sum over n, ho, wo of the input
+    under tap (r, s) times dy[n,ho,wo,k].  dtype "bf16" or "fp32"; a bf16
+    plan writes dw in bf16, or in fp32 with out_fp32=True."""
+
+    def __init__(self, N, H, W, C, K, R, S, stride=1, padding="SAME", dtype="bf16",
+                 out_fp32=False):
+        sh, sw = (stride, stride) if isinstance(stride, int) else stride
+        d = _abi.FconvDesc()
+        d.N, d.H, d.W, d.C, d.K, d.R, d.S = N, H, W, C, K, R, S
+        d.stride_h, d.stride_w = sh, sw
+        d.padding = PADDINGS[padding.upper()] if isinstance(padding, str) else padding
+        d.dtype = DTYPES[dtype] if isinstance(dtype, str) else dtype
+        d.n_ops = 0
+        d.flags = _abi.FCONV_WGRAD_OUT_FP32 if out_fp32 else 0
+        self.desc = d
+        self.dtype = dtype
+        self.out_dtype = "fp32" if (out_fp32 or dtype == "fp32") else dtype
+        self._h = ctypes.c_void_p()
+        _check(_abi.lib().fconv_wgrad_plan_create(ctypes.byref(d), ctypes.byref(self._h)),
+               "fconv_wgrad_plan_create")
+        ho, wo = ctypes.c_int32(), ctypes.c_int32()
+        pads = (ctypes.c_int32 * 4)()
+        _check(_abi.lib().fconv_wgrad_plan_output_dims(self._h, ctypes.byref(ho),
+                                                       ctypes.byref(wo), pads),
+               "fconv_wgrad_plan_output_dims")
+        self.Ho, self.Wo = ho.value, wo.value
+        self.pads = tuple(pads)
+        nbytes = ctypes.c_size_t()
+        _check(_abi.lib().fconv_wgrad_plan_workspace_size(self._h, ctypes.byref(nbytes)),
+               "fconv_wgrad_plan_workspace_size")
+        self.workspace_bytes = nbytes.value
+        self.kernel_name = _abi.lib().fconv_wgrad_plan_kernel_name(self._h).decode()
+        self.dy_shape = (N, self.Ho, self.Wo, K)
+        self.dw_shape = (R, S, C, K)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _abi.lib().fconv_wgrad_plan_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    def run_raw(self, x, dy, dw, workspace, workspace_bytes=None, stream=None) -> int:
+        """Enqueue; returns the raw status (no exception)."""
+        if workspace_bytes is None:
+            workspace_bytes = (workspace.numel() * workspace.element_size()
+                               if hasattr(workspace, "numel") else self.workspace_bytes)
+        ptrs = (_addr(x), _addr(dy), _addr(dw), _addr(workspace))
+        return _abi.lib().fconv_wgrad_plan_run(self._h, _stream_handle(stream), *ptrs,
+                                               workspace_bytes)
+
+    def run(self, x, dy, dw, workspace, stream=None):
+        _check(self.run_raw(x, dy, dw, workspace, stream=stream), "fconv_wgrad_plan_run")
+        return dw
+
+    def __call__(self, x, dy, stream=None):
+        """Allocate dw and the workspace with torch, run, return dw."""
+        import torch
+        tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[self.out_dtype]
+        dw = torch.empty(self.dw_shape, dtype=tdt, device=x.device)
+        ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=x.device)
+        return self.run(x, dy, dw, ws, stream=stream)
 
 
 def autotune_cache_clear():

@@ -20,12 +20,16 @@ OP_LEAKY_RELU, OP_CLIPPED_RELU, OP_CLAMP = 6, 7, 8
 FCONV_MAX_OPS = 8
 FCONV_RUN_FILTER_PREPACKED = 1
 FCONV_DESC_CUDNN7_ORDER = 1
+FCONV_WGRAD_OUT_FP32 = 1
 
 # Every symbol include/fconv.h declares.
 EXPORTS = ("fconv_plan_create", "fconv_plan_output_dims", "fconv_plan_workspace_size",
            "fconv_plan_pack_filter", "fconv_plan_run", "fconv_plan_destroy",
            "fconv_plan_kernel_name", "fconv_status_string", "fconv_plan_autotune",
-           "fconv_autotune_cache_clear")
+           "fconv_autotune_cache_clear", "fconv_wgrad_plan_create",
+           "fconv_wgrad_plan_output_dims", "fconv_wgrad_plan_workspace_size",
+           "fconv_wgrad_plan_run", "fconv_wgrad_plan_kernel_name",
+           "fconv_wgrad_plan_destroy")
 
 
 class FconvDesc(ctypes.Structure):
@@ -87,6 +91,20 @@ def lib():
         L.fconv_plan_autotune.restype = st
         L.fconv_autotune_cache_clear.argtypes = []
         L.fconv_autotune_cache_clear.restype = None
+        L.fconv_wgrad_plan_create.argtypes = [ctypes.POINTER(FconvDesc), ctypes.POINTER(P)]
+        L.fconv_wgrad_plan_create.restype = st
+        L.fconv_wgrad_plan_output_dims.argtypes = [P, ctypes.POINTER(ctypes.c_int32),
+                                                   ctypes.POINTER(ctypes.c_int32),
+                                                   ctypes.POINTER(ctypes.c_int32)]
+        L.fconv_wgrad_plan_output_dims.restype = st
+        L.fconv_wgrad_plan_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        L.fconv_wgrad_plan_workspace_size.restype = st
+        L.fconv_wgrad_plan_run.argtypes = [P, P, P, P, P, P, ctypes.c_size_t]
+        L.fconv_wgrad_plan_run.restype = st
+        L.fconv_wgrad_plan_kernel_name.argtypes = [P]
+        L.fconv_wgrad_plan_kernel_name.restype = ctypes.c_char_p
+        L.fconv_wgrad_plan_destroy.argtypes = [P]
+        L.fconv_wgrad_plan_destroy.restype = st
         L.fconv_status_string.argtypes = [st]
         L.fconv_status_string.restype = ctypes.c_char_p
         _lib = L

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libfconv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "conv.hip"]
+SOURCES = ["plan.cpp", "conv.hip", "wgrad.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-Wall", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC]

@@ -24,27 +24,6 @@ using namespace fconv;
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// Output size and padding.  SAME: TensorFlow conv_ops_fused_int8.cc,
-// LaunchFusedConv2DOpGpuInt8Helper -- the total padding is
-// max(0, (out-1)*stride + filter - in), half of it (rounded down) before and
-// the rest after; the output size is ceil(in / stride).  VALID: no padding.
-bool resolve_axis(int32_t in, int32_t f, int32_t stride, bool same, int32_t* out,
-                  int32_t* before, int32_t* after) {
-  if (same) {
-    int64_t o = (static_cast<int64_t>(in) + stride - 1) / stride;
-    int64_t total = (o - 1) * stride + f - in;
-    if (total < 0) total = 0;
-    *out = static_cast<int32_t>(o);
-    *before = static_cast<int32_t>(total / 2);
-    *after = static_cast<int32_t>(total - total / 2);
-    return true;
-  }
-  if (in < f) return false;
-  *out = (in - f) / stride + 1;
-  *before = *after = 0;
-  return true;
-}
-
 // Accepted operator sequences; see the fconv_op comment in fconv.h.
 fconv_status parse_ops(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
@@ -279,6 +258,27 @@ FastDiv make_fast_div(uint32_t d) {
   while ((uint64_t{1} << s) < d) ++s;
   const uint64_t m = ((uint64_t{1} << (32 + s)) / d) + 1;
   return FastDiv{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), s};
+}
+
+// Output size and padding.  SAME: TensorFlow conv_ops_fused_int8.cc,
+// LaunchFusedConv2DOpGpuInt8Helper -- the total padding is
+// max(0, (out-1)*stride + filter - in), half of it (rounded down) before and
+// the rest after; the output size is ceil(in / stride).  VALID: no padding.
+bool resolve_axis(int32_t in, int32_t f, int32_t stride, bool same, int32_t* out,
+                  int32_t* before, int32_t* after) {
+  if (same) {
+    int64_t o = (static_cast<int64_t>(in) + stride - 1) / stride;
+    int64_t total = (o - 1) * stride + f - in;
+    if (total < 0) total = 0;
+    *out = static_cast<int32_t>(o);
+    *before = static_cast<int32_t>(total / 2);
+    *after = static_cast<int32_t>(total - total / 2);
+    return true;
+  }
+  if (in < f) return false;
+  *out = (in - f) / stride + 1;
+  *before = *after = 0;
+  return true;
 }
 
 fconv_status check_pack_args(const fconv_plan_s* p, const void* w,

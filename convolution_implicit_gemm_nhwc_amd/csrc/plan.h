@@ -26,6 +26,11 @@ struct FastDiv {
 };
 FastDiv make_fast_div(uint32_t d);
 
+// Output size and padding along one axis (SAME or VALID); false for VALID
+// with in < f.  Shared by the forward and weight-gradient plans.
+bool resolve_axis(int32_t in, int32_t f, int32_t stride, bool same, int32_t* out,
+                  int32_t* before, int32_t* after);
+
 // How the implicit-GEMM A operand (im2col row) is gathered, per 16-byte
 // chunk of the reduction dimension (r, s, c):
 //   kLoadTap:   C is a multiple of one k-step, so a whole k-step sits in one

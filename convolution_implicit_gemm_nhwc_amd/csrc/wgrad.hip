@@ -1,0 +1,635 @@
+// Weight gradient of the NHWC convolution on gfx950 (CDNA4), and its C ABI.
+//
+//   dw[r,s,c,k] = sum over pixels m = (n, ho, wo) of P[m, (r,s,c)] * dy[m, k]
+//   P[m, (r,s,c)] = X(n, ho*sh - pt + r, wo*sw - pl + s, c)   (zero outside)
+//
+// TensorFlow conv_grad_filter_ops.cc (Conv2DCustomBackpropFilterOp) forms,
+// per image, the Im2col patch matrix [Ho*Wo, R*S*C] and multiplies its
+// transpose by the output gradient [Ho*Wo, K].  Here the sum over images is
+// folded into one implicit GEMM whose reduction runs over all M = N*Ho*Wo
+// pixels:
+//   rows   k  = output channel          K
+//   cols   kk = (r, s, c)               Kg = R*S*C   (HWIO row order)
+//   reduction m = (n, ho, wo)           M
+// The patch matrix is never built: each lane gathers 16-byte slices of
+// patch rows straight from the NHWC input (taps in the padding read zero).
+//
+// Matrix-core mapping.  The 16x16 MFMA wants, per lane, a 16-byte run of the
+// reduction index for one row (A) and one column (B).  Both operands arrive
+// pixel-major (NHWC: the channels of one pixel are contiguous), so the
+// loader transposes in registers: a lane fetches the same 16-byte channel
+// chunk of E consecutive pixels (E = 8 bf16 / 4 fp32), transposes the E x E
+// block, and writes E pixel runs, one per channel, to LDS rows of 128 bytes
+// (one row per channel, one 16-byte slot per E pixels).  Fragment reads are
+// then single ds_read_b128s.  A = dy (rows k), B = patch (cols kk), so a lane
+// ends with 4 consecutive output channels of one (r, s, c): one 16-byte store.
+//
+// Work split.  A workgroup owns a TK x 128 tile of dw over one range of
+// pixels.  When tiles alone do not fill the chip, the pixels are split into
+// ranges; each range writes its fp32 partial tile to the workspace and a
+// second kernel adds the ranges in a fixed order, so the result does not
+// depend on scheduling.  Workgroups of one range are placed on one XCD
+// (blockIdx round-robins over the 8 XCDs), so the range's input and gradient
+// rows are fetched into one L2 and shared by all its tiles.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <limits.h>
+#include <string.h>
+
+#include <new>
+
+#include "plan.h"
+
+struct fconv_wgrad_plan_s {
+  fconv_desc d;
+  int32_t Ho, Wo, pt, pb, pl, pr;
+  int32_t esize;     // bytes per x / dy element
+  int32_t E;         // elements per 16-byte chunk
+  int64_t M;         // N*Ho*Wo, reduction length
+  int32_t Kg;        // R*S*C
+  bool out_fp32;     // dw written as fp32
+  bool vec;          // C % E == 0 and K % E == 0: 16-byte gathers
+  int32_t tk;        // output channels per tile (64 or 128)
+  int32_t tiles_k, tiles_kk;
+  int32_t splits;    // pixel ranges
+  int32_t m_per_split;
+  int64_t lp;        // partial tile stride in floats (Kg*K rounded up to 4)
+  size_t ws_bytes;
+  int64_t x_elems, dy_elems, dw_elems;
+  fconv::FastDiv hw_div, wo_div;
+  const char* kernel_name;
+};
+
+namespace fconv {
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWgThreads = 256;   // 4 waves
+constexpr int kWgTKK = 128;       // (r,s,c) columns per tile
+constexpr int kWgRowBytes = 128;  // one LDS row: 8 slots of 16 bytes
+constexpr int kWgTargetBlocks = 512;  // about two workgroups per CU
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every extent: reads 0
+constexpr int kBufferDword3 = 0x00020000;      // raw buffer descriptor, gfx9 family
+
+struct WgArgs {
+  const void* x;
+  const void* dy;
+  void* out;  // partial sums [split][lp] fp32, or dw
+  int32_t N, H, W, C, K, R, S, sh, sw, pt, pl, Ho, Wo;
+  int32_t M, Kg;
+  int32_t tiles_k, tiles_kk, splits, m_per_split;
+  int32_t blocks;  // splits * tiles_k * tiles_kk
+  int32_t out_mode;  // 0 partial fp32, 1 dw fp32, 2 dw bf16
+  int64_t lp;
+  uint32_t x_bytes, dy_bytes;
+  uint32_t hw_mul, hw_add, hw_shift, wo_mul, wo_add, wo_shift;
+};
+
+__device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint32_t shift) {
+  return (__umulhi(n, mul) + (add ? n : 0u)) >> shift;
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferDword3);
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// One 16-byte fragment pair through the matrix core: 8 bf16 per lane (one
+// instruction) or 4 fp32 per lane (four instructions, one element each).
+template <int DT>
+__device__ inline f32x4 wg_mma(i32x4 a, i32x4 b, f32x4 c) {
+  if constexpr (DT == FCONV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    // Bit-cast whole vectors, then index (a bit-cast of one ext-vector
+    // element reads element 0 in this compiler).
+    const f32x4 af = __builtin_bit_cast(f32x4, a);
+    const f32x4 bf = __builtin_bit_cast(f32x4, b);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af.x, bf.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af.y, bf.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af.z, bf.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af.w, bf.w, c, 0, 0, 0);
+    return c;
+  }
+}
+
+// Slot of pixel run `chunk` in LDS row `row`.  Rows are 128 bytes; the
+// xor with the row's low bits spreads the 16 rows one fragment read touches
+// over all eight slots, and the xor with bits 3..5 does the same for the
+// rows one transposed write touches (E apart).
+__device__ inline int wg_slot(int row, int chunk) {
+  return chunk ^ ((row ^ (row >> 3)) & 7);
+}
+
+// Transpose an E x E block held as E chunks (chunk e = pixel e's E channels)
+// into E chunks (chunk j = channel j's E pixels).
+template <int DT, int E>
+__device__ inline void wg_transpose(const i32x4 (&v)[E], i32x4 (&o)[E]) {
+  if constexpr (DT == FCONV_BF16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[j][d] = static_cast<int32_t>(__builtin_amdgcn_perm(
+            static_cast<uint32_t>(v[2 * d + 1][j >> 1]), static_cast<uint32_t>(v[2 * d][j >> 1]),
+            sel));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[j][e] = v[e][j];
+  }
+}
+
+// Main kernel.  DT: bf16 or fp32.  TK: output channels per tile (64 / 128).
+// VEC: C and K are multiples of E, so every gathered chunk is one 16-byte
+// load; otherwise elements are gathered one by one (any shape).
+//
+// Per stage (BM = 8*E pixels): every thread fetches its tasks' chunks (one
+// task = one 16-byte column chunk x E pixels of dy or of the patch matrix),
+// transposes them and writes them to the stage's LDS buffer; a barrier; the
+// four waves (a 2x2 or 1x4 grid over the tile) then run the stage's MFMAs
+// while the next stage's chunks are in flight.  Two LDS buffers alternate.
+template <int DT, int TK, bool VEC>
+__global__ __launch_bounds__(kWgThreads) void wgrad_kernel(WgArgs a) {
+  constexpr int ES = DT == FCONV_BF16 ? 2 : 4;
+  constexpr int E = 16 / ES;
+  constexpr int BM = 8 * E;                  // pixels per stage
+  constexpr int ROWS = TK + kWgTKK;          // LDS rows per stage
+  constexpr int NT_DY = (TK / E) * 8;        // dy tasks per stage
+  constexpr int NT = NT_DY + (kWgTKK / E) * 8;
+  constexpr int TPT = (NT + kWgThreads - 1) / kWgThreads;  // tasks per thread
+  constexpr int WK = TK / 64;                // waves along k (1 or 2)
+  constexpr int WKK = 4 / WK;                // waves along kk (4 or 2)
+  constexpr int NI = 4;                      // 16-row MFMA tiles per wave along k
+  constexpr int NJ = kWgTKK / WKK / 16;      // along kk (2 or 4)
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * kWgRowBytes];
+
+  // Block -> (pixel range, tile).  Consecutive logical ids share a pixel
+  // range; the remap puts consecutive ids on one XCD when the grid is a
+  // multiple of 8 (the launcher pads it so).
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  if (logical >= a.blocks) return;
+  const int tiles = a.tiles_k * a.tiles_kk;
+  const int split = logical / tiles;
+  const int tile = logical % tiles;
+  const int k0 = (tile % a.tiles_k) * TK;
+  const int kk0 = (tile / a.tiles_k) * kWgTKK;
+  const int m_begin = split * a.m_per_split;
+  const int m_end = min(a.M, m_begin + a.m_per_split);
+  const int nst = (m_end - m_begin + BM - 1) / BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wk = wave % WK, wkk = wave / WK;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
+
+  // Per-task constants (a thread's tasks keep their column chunk across
+  // stages; only the pixels move).
+  int t_isdy[TPT], t_cc[TPT], t_pc[TPT], t_col[TPT], t_r[TPT], t_s[TPT], t_c[TPT];
+  bool t_on[TPT];
+#pragma unroll
+  for (int i = 0; i < TPT; ++i) {
+    const int t = tid + i * kWgThreads;
+    t_on[i] = t < NT;
+    const bool isdy = t < NT_DY;
+    const int local = isdy ? t : t - NT_DY;
+    const int ncc = (isdy ? TK : kWgTKK) / E;
+    t_isdy[i] = isdy;
+    t_cc[i] = local % ncc;
+    t_pc[i] = local / ncc;
+    t_col[i] = (isdy ? k0 : kk0) + t_cc[i] * E;  // first channel k / column kk
+    t_r[i] = t_s[i] = t_c[i] = 0;
+    if (!isdy && VEC) {
+      const int rs = t_col[i] / a.C;
+      t_c[i] = t_col[i] - rs * a.C;
+      t_r[i] = rs / a.S;
+      t_s[i] = rs - t_r[i] * a.S;
+    }
+  }
+
+  // Element offset of input pixel (n, ho*sh - pt + r, wo*sw - pl + s), or -1
+  // outside the image / past the pixel range.
+  auto patch_pixel = [&](int m, int r, int s) -> int64_t {
+    if (m >= m_end) return -1;
+    const uint32_t n = fast_div(static_cast<uint32_t>(m), a.hw_mul, a.hw_add, a.hw_shift);
+    const uint32_t rem = static_cast<uint32_t>(m) - n * static_cast<uint32_t>(a.Ho * a.Wo);
+    const uint32_t ho = fast_div(rem, a.wo_mul, a.wo_add, a.wo_shift);
+    const uint32_t wo = rem - ho * static_cast<uint32_t>(a.Wo);
+    const int hi = static_cast<int>(ho) * a.sh - a.pt + r;
+    const int wi = static_cast<int>(wo) * a.sw - a.pl + s;
+    if (hi < 0 || hi >= a.H || wi < 0 || wi >= a.W) return -1;
+    return ((static_cast<int64_t>(n) * a.H + hi) * a.W + wi);
+  };
+
+  i32x4 reg[TPT][E];
+  auto fetch = [&](int st) {
+    const int mb = m_begin + st * BM;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int m = mb + t_pc[i] * E + e;
+        if constexpr (VEC) {
+          uint32_t off = kOutOfRange;
+          if (t_on[i]) {
+            if (t_isdy[i]) {
+              if (m < m_end && t_col[i] < a.K)
+                off = static_cast<uint32_t>((static_cast<int64_t>(m) * a.K + t_col[i]) * ES);
+            } else if (t_col[i] < a.Kg) {
+              const int64_t px = patch_pixel(m, t_r[i], t_s[i]);
+              if (px >= 0) off = static_cast<uint32_t>((px * a.C + t_c[i]) * ES);
+            }
+          }
+          // Every wave's tasks are all dy or all patch (the task counts are
+          // multiples of 64), so the descriptor choice is wave-uniform.
+          const bool dy_task = __builtin_amdgcn_readfirstlane(t_isdy[i]) != 0;
+          reg[i][e] = __builtin_amdgcn_raw_buffer_load_b128(dy_task ? dr : xr, off, 0, 0);
+        } else {
+          // Element by element: column j of the chunk is channel / column
+          // t_col + j, each with its own bounds (and tap for the patch).
+          union {
+            i32x4 v;
+            uint16_t h[8];
+            float f[4];
+          } u;
+          u.v = i32x4{0, 0, 0, 0};
+          if (t_on[i] && m < m_end) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+              const int col = t_col[i] + j;
+              int64_t idx = -1;
+              if (t_isdy[i]) {
+                if (col < a.K) idx = static_cast<int64_t>(m) * a.K + col;
+              } else if (col < a.Kg) {
+                const int rs = col / a.C;
+                const int c = col - rs * a.C;
+                const int r = rs / a.S;
+                const int64_t px = patch_pixel(m, r, rs - r * a.S);
+                if (px >= 0) idx = px * a.C + c;
+              }
+              if (idx >= 0) {
+                if constexpr (DT == FCONV_BF16)
+                  u.h[j] = (t_isdy[i] ? static_cast<const uint16_t*>(a.dy)
+                                      : static_cast<const uint16_t*>(a.x))[idx];
+                else
+                  u.f[j] = (t_isdy[i] ? static_cast<const float*>(a.dy)
+                                      : static_cast<const float*>(a.x))[idx];
+              }
+            }
+          }
+          reg[i][e] = u.v;
+        }
+      }
+    }
+  };
+
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      if (!t_on[i]) continue;
+      i32x4 o[E];
+      wg_transpose<DT, E>(reg[i], o);
+      const int row0 = (t_isdy[i] ? 0 : TK) + t_cc[i] * E;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int row = row0 + j;
+        *reinterpret_cast<i32x4*>(&lds[buf][row * kWgRowBytes + wg_slot(row, t_pc[i]) * 16]) =
+            o[j];
+      }
+    }
+  };
+
+  f32x4 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int arow0 = wk * 64 + (lane & 15);
+  const int brow0 = TK + wkk * (NJ * 16) + (lane & 15);
+  const int g = lane >> 4;
+
+  if (nst > 0) fetch(0);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    stash(buf);
+    if (st + 1 < nst) fetch(st + 1);
+    __syncthreads();
+    // Two k-steps per stage: k-step q reads pixel runs 4q .. 4q+3.
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int chunk = 4 * q + g;
+      i32x4 af[NI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = arow0 + 16 * i;
+        af[i] = *reinterpret_cast<const i32x4*>(
+            &lds[buf][row * kWgRowBytes + wg_slot(row, chunk) * 16]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int row = brow0 + 16 * j;
+        bfr[j] = *reinterpret_cast<const i32x4*>(
+            &lds[buf][row * kWgRowBytes + wg_slot(row, chunk) * 16]);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = wg_mma<DT>(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+  // Lane holds D[k][kk] for k = kbase + 4g + t (t = 0..3), kk = kkbase + lane%16.
+  const bool kvec4 = (a.K & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = k0 + wk * 64 + 16 * i + 4 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kk = kk0 + wkk * (NJ * 16) + 16 * j + (lane & 15);
+      if (kk >= a.Kg || k >= a.K) continue;
+      const f32x4 v = acc[i][j];
+      const int64_t base = static_cast<int64_t>(kk) * a.K + k;
+      if (a.out_mode == 0) {
+        float* o = static_cast<float*>(a.out) + split * a.lp + base;
+        if (kvec4) {
+          *reinterpret_cast<f32x4*>(o) = v;
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
+        }
+      } else if (a.out_mode == 1) {
+        float* o = static_cast<float*>(a.out) + base;
+        if (kvec4) {
+          *reinterpret_cast<f32x4*>(o) = v;
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
+        }
+      } else {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + base;
+        if (kvec4) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+          *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = f32_to_bf16_rne(v[t]);
+        }
+      }
+    }
+  }
+}
+
+// dw[i] = sum over pixel ranges z of part[z][i], in a fixed association
+// (zeros for no range).  A workgroup owns 16 four-element columns; its 16
+// lane groups each add the ranges z = g, g + 16, g + 32, ... in increasing
+// order, and the 16 group sums are then added in group order.  Many ranges
+// are thus read in parallel (the sum is bound by the partials' bandwidth,
+// not by the latency of one long chain), and every run adds the same values
+// in the same order.
+constexpr int kRedCols = 16;    // four-element columns per workgroup
+constexpr int kRedGroups = 16;  // lane groups over the ranges
+
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ part,
+                                                           void* __restrict__ dw, int splits,
+                                                           int64_t lp, int64_t L, int out_bf16) {
+  __shared__ f32x4 red[kRedGroups][kRedCols];
+  const int col = threadIdx.x % kRedCols;
+  const int g = threadIdx.x / kRedCols;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kRedCols + col) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (i0 < L) {
+    for (int z = g; z < splits; z += kRedGroups)
+      s += *reinterpret_cast<const f32x4*>(part + z * lp + i0);
+  }
+  red[g][col] = s;
+  __syncthreads();
+  if (g != 0 || i0 >= L) return;
+  s = red[0][col];
+#pragma unroll
+  for (int q = 1; q < kRedGroups; ++q) s += red[q][col];
+  if (out_bf16) {
+    uint16_t* o = static_cast<uint16_t*>(dw) + i0;
+    if (i0 + 4 <= L && (L & 3) == 0) {
+      const uint32_t lo = f32_to_bf16_rne(s[0]) | (uint32_t(f32_to_bf16_rne(s[1])) << 16);
+      const uint32_t hi = f32_to_bf16_rne(s[2]) | (uint32_t(f32_to_bf16_rne(s[3])) << 16);
+      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    } else {
+      for (int t = 0; t < 4 && i0 + t < L; ++t) o[t] = f32_to_bf16_rne(s[t]);
+    }
+  } else {
+    float* o = static_cast<float*>(dw) + i0;
+    if (i0 + 4 <= L && (L & 3) == 0) {
+      *reinterpret_cast<f32x4*>(o) = s;
+    } else {
+      for (int t = 0; t < 4 && i0 + t < L; ++t) o[t] = s[t];
+    }
+  }
+}
+
+template <int DT, int TK, bool VEC>
+hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
+  const int grid = (a.blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL((wgrad_kernel<DT, TK, VEC>), dim3(grid), dim3(kWgThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
+  if (p->tk == 128)
+    return p->vec ? launch_wgrad_main<DT, 128, true>(a, s) : launch_wgrad_main<DT, 128, false>(a, s);
+  return p->vec ? launch_wgrad_main<DT, 64, true>(a, s) : launch_wgrad_main<DT, 64, false>(a, s);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+const char* wgrad_kernel_name(int dtype, int tk, bool vec) {
+  if (dtype == FCONV_BF16)
+    return tk == 128 ? (vec ? "wgrad_bf16_128" : "wgrad_bf16_128_elem")
+                     : (vec ? "wgrad_bf16_64" : "wgrad_bf16_64_elem");
+  return tk == 128 ? (vec ? "wgrad_f32_128" : "wgrad_f32_128_elem")
+                   : (vec ? "wgrad_f32_64" : "wgrad_f32_64_elem");
+}
+
+}  // namespace
+}  // namespace fconv
+
+extern "C" {
+
+fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* out) {
+  using namespace fconv;
+  if (!desc || !out) return FCONV_ERR_INVALID_ARG;
+  *out = nullptr;
+  const fconv_desc& d = *desc;
+  if (d.dtype != FCONV_BF16 && d.dtype != FCONV_FP32) return FCONV_ERR_UNSUPPORTED;
+  if (d.padding != FCONV_PAD_SAME && d.padding != FCONV_PAD_VALID) return FCONV_ERR_UNSUPPORTED;
+  if (d.n_ops != 0 || (d.flags & ~FCONV_WGRAD_OUT_FP32)) return FCONV_ERR_UNSUPPORTED;
+  if (d.N < 0 || d.H < 1 || d.W < 1 || d.C < 1 || d.K < 1 || d.R < 1 || d.S < 1 ||
+      d.stride_h < 1 || d.stride_w < 1)
+    return FCONV_ERR_INVALID_ARG;
+  fconv_wgrad_plan_s* p = new (std::nothrow) fconv_wgrad_plan_s();
+  if (!p) return FCONV_ERR_INVALID_ARG;
+  p->d = d;
+  const bool same = d.padding == FCONV_PAD_SAME;
+  if (!resolve_axis(d.H, d.R, d.stride_h, same, &p->Ho, &p->pt, &p->pb) ||
+      !resolve_axis(d.W, d.S, d.stride_w, same, &p->Wo, &p->pl, &p->pr)) {
+    delete p;
+    return FCONV_ERR_INVALID_ARG;
+  }
+  p->esize = d.dtype == FCONV_BF16 ? 2 : 4;
+  p->E = 16 / p->esize;
+  p->out_fp32 = d.dtype == FCONV_FP32 || (d.flags & FCONV_WGRAD_OUT_FP32) != 0;
+  p->M = static_cast<int64_t>(d.N) * p->Ho * p->Wo;
+  p->x_elems = static_cast<int64_t>(d.N) * d.H * d.W * d.C;
+  p->dy_elems = p->M * d.K;
+  const int64_t kg = static_cast<int64_t>(d.R) * d.S * d.C;
+  p->dw_elems = kg * d.K;
+  // Buffer descriptors and offsets are 32-bit.
+  if (p->x_elems * p->esize >= INT32_MAX || p->dy_elems * p->esize >= INT32_MAX ||
+      p->dw_elems >= INT32_MAX / 4 || p->M >= INT32_MAX) {
+    delete p;
+    return FCONV_ERR_UNSUPPORTED;
+  }
+  p->Kg = static_cast<int32_t>(kg);
+  p->vec = d.C % p->E == 0 && d.K % p->E == 0;
+  p->tk = d.K > 64 ? 128 : 64;
+  p->tiles_k = (d.K + p->tk - 1) / p->tk;
+  p->tiles_kk = (p->Kg + kWgTKK - 1) / kWgTKK;
+  const int64_t tiles = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
+  const int64_t bm = 8 * p->E;
+  // Pixel ranges: enough workgroups for about two per CU, each range at
+  // least four stages long.
+  int64_t splits = (kWgTargetBlocks + tiles - 1) / tiles;
+  const int64_t max_splits = (p->M + 4 * bm - 1) / (4 * bm);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t mps = (p->M + splits - 1) / splits;
+  mps = (mps + bm - 1) / bm * bm;
+  if (mps < bm) mps = bm;
+  splits = (p->M + mps - 1) / mps;
+  if (splits < 1) splits = 1;
+  if (splits * tiles >= INT32_MAX) {
+    delete p;
+    return FCONV_ERR_UNSUPPORTED;
+  }
+  p->splits = static_cast<int32_t>(splits);
+  p->m_per_split = static_cast<int32_t>(mps);
+  p->lp = (p->dw_elems + 3) / 4 * 4;
+  p->ws_bytes = splits > 1 ? static_cast<size_t>(splits * p->lp * 4) : 0;
+  p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
+  p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
+  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec);
+  *out = p;
+  return FCONV_OK;
+}
+
+fconv_status fconv_wgrad_plan_output_dims(fconv_wgrad_plan p, int32_t* Ho, int32_t* Wo,
+                                          int32_t pads_tblr[4]) {
+  if (!p) return FCONV_ERR_INVALID_ARG;
+  if (Ho) *Ho = p->Ho;
+  if (Wo) *Wo = p->Wo;
+  if (pads_tblr) {
+    pads_tblr[0] = p->pt;
+    pads_tblr[1] = p->pb;
+    pads_tblr[2] = p->pl;
+    pads_tblr[3] = p->pr;
+  }
+  return FCONV_OK;
+}
+
+fconv_status fconv_wgrad_plan_workspace_size(fconv_wgrad_plan p, size_t* bytes) {
+  if (!p || !bytes) return FCONV_ERR_INVALID_ARG;
+  *bytes = p->ws_bytes;
+  return FCONV_OK;
+}
+
+fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan p, void* stream, const void* x,
+                                  const void* dy, void* dw, void* workspace,
+                                  size_t workspace_bytes) {
+  using namespace fconv;
+  if (!p || !x || !dy || !dw) return FCONV_ERR_INVALID_ARG;
+  if (p->ws_bytes > 0 && (!workspace || workspace_bytes < p->ws_bytes)) return FCONV_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dw) ||
+      (p->ws_bytes > 0 && !aligned16(workspace)))
+    return FCONV_ERR_MISALIGNED;
+  const size_t xb = static_cast<size_t>(p->x_elems) * p->esize;
+  const size_t db = static_cast<size_t>(p->dy_elems) * p->esize;
+  const size_t wb = static_cast<size_t>(p->dw_elems) * (p->out_fp32 ? 4 : 2);
+  if (overlaps(dw, wb, x, xb) || overlaps(dw, wb, dy, db) ||
+      overlaps(dw, wb, workspace, p->ws_bytes) || overlaps(workspace, p->ws_bytes, x, xb) ||
+      overlaps(workspace, p->ws_bytes, dy, db))
+    return FCONV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t L = p->dw_elems;
+  const int reduce_grid = static_cast<int>((L + 4 * kRedCols - 1) / (4 * kRedCols));
+  const int out_bf16 = p->out_fp32 ? 0 : 1;
+  if (p->M == 0) {
+    // Empty batch: the gradient is zero.
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(reduce_grid), dim3(256), 0, s,
+                       static_cast<const float*>(nullptr), dw, 0, p->lp, L, out_bf16);
+    return hipGetLastError() == hipSuccess ? FCONV_OK : FCONV_ERR_DEVICE;
+  }
+  WgArgs a;
+  a.x = x;
+  a.dy = dy;
+  a.out = p->splits > 1 ? workspace : dw;
+  a.N = p->d.N; a.H = p->d.H; a.W = p->d.W; a.C = p->d.C; a.K = p->d.K;
+  a.R = p->d.R; a.S = p->d.S; a.sh = p->d.stride_h; a.sw = p->d.stride_w;
+  a.pt = p->pt; a.pl = p->pl; a.Ho = p->Ho; a.Wo = p->Wo;
+  a.M = static_cast<int32_t>(p->M);
+  a.Kg = p->Kg;
+  a.tiles_k = p->tiles_k;
+  a.tiles_kk = p->tiles_kk;
+  a.splits = p->splits;
+  a.m_per_split = p->m_per_split;
+  a.blocks = p->splits * p->tiles_k * p->tiles_kk;
+  a.out_mode = p->splits > 1 ? 0 : (p->out_fp32 ? 1 : 2);
+  a.lp = p->lp;
+  a.x_bytes = static_cast<uint32_t>(xb);
+  a.dy_bytes = static_cast<uint32_t>(db);
+  a.hw_mul = p->hw_div.mul; a.hw_add = p->hw_div.add; a.hw_shift = p->hw_div.shift;
+  a.wo_mul = p->wo_div.mul; a.wo_add = p->wo_div.add; a.wo_shift = p->wo_div.shift;
+  hipError_t e = p->d.dtype == FCONV_BF16 ? launch_wgrad_dt<FCONV_BF16>(p, a, s)
+                                           : launch_wgrad_dt<FCONV_FP32>(p, a, s);
+  if (e != hipSuccess) return FCONV_ERR_DEVICE;
+  if (p->splits > 1) {
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(reduce_grid), dim3(256), 0, s,
+                       static_cast<const float*>(workspace), dw, p->splits, p->lp, L, out_bf16);
+    if (hipGetLastError() != hipSuccess) return FCONV_ERR_DEVICE;
+  }
+  return FCONV_OK;
+}
+
+const char* fconv_wgrad_plan_kernel_name(fconv_wgrad_plan p) { return p ? p->kernel_name : nullptr; }
+
+fconv_status fconv_wgrad_plan_destroy(fconv_wgrad_plan p) {
+  delete p;
+  return FCONV_OK;
+}
+
+}  // extern "C"

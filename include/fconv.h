@@ -251,6 +251,73 @@ FCONV_API const char* fconv_plan_kernel_name(fconv_plan plan);
 /* Static, human-readable text for a status code. */
 FCONV_API const char* fconv_status_string(fconv_status status);
 
+/* ------------------------------------------------------------------------
+ * Weight gradient (filter gradient) of the same convolution.
+ *
+ *   dw[r,s,c,k] = sum_{n<N, ho<Ho, wo<Wo} X(n, ho*sh - pt + r, wo*sw - pl + s, c)
+ *                                          * dy[n,ho,wo,k]
+ *
+ * with X, the strides and the SAME/VALID padding exactly as in the forward
+ * convolution above.  TensorFlow conv_grad_filter_ops.cc
+ * (Conv2DCustomBackpropFilterOp) computes it per image as the Im2col patch
+ * matrix transposed times the output gradient, [R*S*C, Ho*Wo] x [Ho*Wo, K],
+ * summed over the images; here it is one implicit GEMM whose reduction runs
+ * over all N*Ho*Wo output pixels, the patch matrix never materialised.
+ *
+ * The plan is created from an fconv_desc that describes the forward
+ * convolution (N, H, W, C, K, R, S, strides, padding, dtype); n_ops must be 0.
+ * dtype FCONV_BF16 or FCONV_FP32 (FCONV_INT8 is FCONV_ERR_UNSUPPORTED: the
+ * int8 op has no gradient on the pages).  Products are exact and sums are
+ * fp32 (matrix-core accumulation, then a fixed-order sum over pixel ranges),
+ * so the result is deterministic: the same inputs give the same bits on every
+ * run.  dw is written in the plan dtype (bf16 rounded to nearest even), or in
+ * fp32 for a bf16 plan created with FCONV_WGRAD_OUT_FP32.
+ * ------------------------------------------------------------------------ */
+
+typedef struct fconv_wgrad_plan_s* fconv_wgrad_plan;
+
+/* Descriptor flag of fconv_wgrad_plan_create: a bf16 plan writes dw as fp32
+ * (the fp32 sums, unrounded).  No effect on an fp32 plan. */
+#define FCONV_WGRAD_OUT_FP32 1u
+
+/* Validates the descriptor and resolves Ho, Wo and the padding as
+ * fconv_plan_create does; picks the tiling and how many pixel ranges the
+ * reduction is split into.  Host only.  Errors: FCONV_ERR_INVALID_ARG (NULL
+ * pointer, non-positive size or stride, VALID with H < R or W < S),
+ * FCONV_ERR_UNSUPPORTED (dtype not bf16/fp32, n_ops != 0, unknown flags, x or
+ * dy of 2 GiB or more). */
+FCONV_API fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* out);
+
+/* Shape of dy, [N][Ho][Wo][K], and the resolved padding (top, bottom, left,
+ * right).  Any output pointer may be NULL. */
+FCONV_API fconv_status fconv_wgrad_plan_output_dims(fconv_wgrad_plan plan, int32_t* Ho,
+                                                    int32_t* Wo, int32_t pads_tblr[4]);
+
+/* Bytes of workspace a run needs: the fp32 partial sums of the pixel ranges
+ * (0 when the reduction is not split). */
+FCONV_API fconv_status fconv_wgrad_plan_workspace_size(fconv_wgrad_plan plan, size_t* bytes);
+
+/* Enqueues dw = the weight gradient on `stream` and returns.
+ *   x   device, NHWC [N][H][W][C] of the plan dtype
+ *   dy  device, NHWC [N][Ho][Wo][K] of the plan dtype
+ *   dw  device, HWIO [R][S][C][K], plan dtype or fp32 (FCONV_WGRAD_OUT_FP32);
+ *       overwritten (zeros when N == 0); must not overlap x, dy or the
+ *       workspace
+ *   workspace / workspace_bytes: device scratch of at least
+ *       fconv_wgrad_plan_workspace_size bytes (may be NULL when that is 0)
+ * Pointers 16-byte aligned.  All checks happen before anything is enqueued.
+ * Errors: FCONV_ERR_INVALID_ARG (NULL plan or tensor, overlap),
+ * FCONV_ERR_MISALIGNED, FCONV_ERR_WORKSPACE, FCONV_ERR_DEVICE. */
+FCONV_API fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan plan, void* stream, const void* x,
+                                            const void* dy, void* dw, void* workspace,
+                                            size_t workspace_bytes);
+
+/* Name of the main kernel the plan launches; NULL for a NULL plan. */
+FCONV_API const char* fconv_wgrad_plan_kernel_name(fconv_wgrad_plan plan);
+
+/* Frees the plan (host memory only).  NULL is a no-op. */
+FCONV_API fconv_status fconv_wgrad_plan_destroy(fconv_wgrad_plan plan);
+
 #ifdef __cplusplus
 }
 #endif

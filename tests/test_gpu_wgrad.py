@@ -1,0 +1,124 @@
+"""Weight-gradient parity: the HIP path (fconv_wgrad_plan_run through the C
+ABI) against the float64 oracle (oracle.wgrad), element by element.
+
+Tolerances on e = max|dw - r| / max|r| (normwise):
+  - fp32 dw (fp32 plans, bf16 plans with out_fp32): 1e-4.  Products of the
+    inputs are exact in fp32 for bf16 and rounded once for fp32; the sums are
+    fp32 over up to 10^5 terms, whose rounding error grows like
+    2^-24 * sqrt(terms) (about 2e-5 at 10^5) for these zero-mean inputs.
+  - bf16 dw: 4e-3, the bf16 rounding of the result (at most 2^-9 of each
+    element, so at most 2^-9 of max|r|) plus the fp32 part.
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_nhwc_amd as fc
+import oracle
+import workloads as wl
+from gpu_helpers import device, float_error, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 4e-3}
+
+
+def draw(rng, shape, dtype):
+    a = rng.normal(0.0, 1.0, size=shape).astype(np.float32)
+    return wl.float_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def run_wgrad(plan, x, dy, dev, fill=None):
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[plan.out_dtype]
+    dw = torch.empty(plan.dw_shape, dtype=tdt, device=dev)
+    if fill is not None:
+        dw.fill_(fill)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    plan.run(to_dev(x, dev), to_dev(dy, dev), dw, ws)
+    torch.cuda.synchronize()
+    return from_dev(dw, plan.out_dtype)
+
+
+# (N, H, W, C, K, R, S, stride, padding): several tiles of both kinds, ragged
+# tails in k, (r, s, c) and pixels, the element-wise gather (C or K off the
+# 16-byte chunk), strides 1-3, SAME and VALID, images smaller than the filter.
+CASES = [
+    (2, 13, 11, 40, 72, 3, 3, 1, "SAME"),
+    (3, 10, 10, 24, 136, 3, 3, 2, "SAME"),
+    (2, 9, 9, 16, 64, 1, 1, 1, "VALID"),
+    (1, 17, 15, 32, 48, 5, 5, 3, "VALID"),
+    (2, 7, 6, 3, 5, 3, 3, 1, "SAME"),
+    (2, 8, 9, 6, 10, 2, 3, 2, "SAME"),
+    (1, 2, 3, 8, 16, 5, 5, 1, "SAME"),
+    (4, 20, 20, 64, 64, 3, 3, 1, "SAME"),
+    (1, 1, 1, 8, 8, 1, 1, 1, "VALID"),
+    (2, 12, 12, 128, 256, 3, 3, 2, "SAME"),
+]
+
+
+@pytest.mark.parametrize("out_fp32", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES)
+def test_wgrad_small_shapes(case, dtype, out_fp32):
+    if dtype == "fp32" and out_fp32:
+        pytest.skip("fp32 plans always write fp32")
+    N, H, W, C, K, R, S, stride, padding = case
+    dev = device()
+    plan = fc.WgradPlan(N, H, W, C, K, R, S, stride, padding, dtype, out_fp32=out_fp32)
+    say("wgrad", case, dtype, "out_fp32" if out_fp32 else "", plan.kernel_name,
+        "ws", plan.workspace_bytes)
+    rng = np.random.default_rng(abs(hash((case, dtype))) % (2 ** 32))
+    x = draw(rng, (N, H, W, C), dtype)
+    dy = draw(rng, plan.dy_shape, dtype)
+    got = run_wgrad(plan, x, dy, dev, fill=7.0)
+    ref = oracle.wgrad(x, dy, R, S, stride, padding)
+    assert got.shape == ref.shape
+    e = float_error(got, ref)
+    assert e <= TOL[plan.out_dtype], (case, dtype, e)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_wgrad_empty_batch_gives_zeros(dtype):
+    dev = device()
+    plan = fc.WgradPlan(0, 8, 8, 16, 32, 3, 3, 1, "SAME", dtype)
+    say("wgrad N=0", dtype)
+    x = torch.empty((0, 8, 8, 16), dtype=torch.float32, device=dev)
+    dy = torch.empty((0, 8, 8, 32), dtype=torch.float32, device=dev)
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[plan.out_dtype]
+    dw = torch.full(plan.dw_shape, 3.0, dtype=tdt, device=dev)
+    # Zero-size tensors have no storage: pass any aligned device address.
+    base = torch.empty(16, dtype=torch.uint8, device=dev)
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    st = plan.run_raw(base.data_ptr(), base.data_ptr(), dw, ws)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert bool((dw == 0).all())
+
+
+def test_wgrad_is_deterministic():
+    dev = device()
+    L = wl.WGRAD_LAYERS["wgrad_3x3_bf16"]
+    inp = wl.make_wgrad_inputs(L, N=4)
+    plan = fc.WgradPlan(4, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, "bf16",
+                        out_fp32=True)
+    say("wgrad determinism", plan.kernel_name, "ws", plan.workspace_bytes)
+    a = run_wgrad(plan, inp.x, inp.dy, dev)
+    b = run_wgrad(plan, inp.x, inp.dy, dev, fill=1.0)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", list(wl.WGRAD_LAYERS))
+def test_wgrad_full_workload(name):
+    """The full benchmark workloads, every element against the oracle."""
+    dev = device()
+    L = wl.WGRAD_LAYERS[name]
+    inp = wl.make_wgrad_inputs(L)
+    plan = fc.WgradPlan(L.N, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
+                        out_fp32=True)
+    assert plan.dy_shape == (L.N, L.Ho, L.Wo, L.K)
+    say("wgrad full", name, plan.kernel_name, "ws", plan.workspace_bytes)
+    got = run_wgrad(plan, inp.x, inp.dy, dev)
+    ref = oracle.wgrad(inp.x, inp.dy, L.R, L.S, L.stride, L.padding)
+    e = float_error(got, ref)
+    say("  normwise error", e)
+    assert e <= TOL["fp32"], (name, e)

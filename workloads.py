@@ -103,6 +103,48 @@ LAYERS = {
 }
 
 
+# Weight-gradient workloads: the filter gradient of a layer's convolution,
+# given its input x and an output gradient dy.  Shapes are those of the
+# forward layers above (the 3x3 bf16/fp32 layer and the 3x3 int8 benchmark
+# layer's geometry run in bf16); ops are empty.
+WGRAD_LAYERS = {
+    "wgrad_3x3_bf16": Layer(
+        "wgrad_3x3_bf16", "bf16", N=16, H=28, W=28, C=256, K=256, R=3, S=3,
+        stride=1, padding="SAME", Ho=28, Wo=28, ops=(), seed=7,
+        description="dW of N=16 28x28x256 -> 256, 3x3 s1 SAME, bf16 in, fp32 dW"),
+    "wgrad_3x3_fp32": Layer(
+        "wgrad_3x3_fp32", "fp32", N=16, H=28, W=28, C=256, K=256, R=3, S=3,
+        stride=1, padding="SAME", Ho=28, Wo=28, ops=(), seed=7,
+        description="dW of N=16 28x28x256 -> 256, 3x3 s1 SAME, fp32"),
+    "wgrad_3x3_64_bf16": Layer(
+        "wgrad_3x3_64_bf16", "bf16", N=32, H=56, W=56, C=64, K=64, R=3, S=3,
+        stride=1, padding="SAME", Ho=56, Wo=56, ops=(), seed=8,
+        description="dW of N=32 56x56x64 -> 64, 3x3 s1 SAME, bf16 in, fp32 dW"),
+}
+
+
+@dataclasses.dataclass
+class WgradInputs:
+    layer: Layer
+    x: np.ndarray   # NHWC, uint16 (bf16 bits) or float32
+    dy: np.ndarray  # NHWC with the output's shape, same dtype
+
+
+def make_wgrad_inputs(layer: Layer, N: Optional[int] = None) -> WgradInputs:
+    """x ~ N(0, 1/sqrt(R*S*C)) as the forward layers draw it, dy ~ N(0, 1);
+    both drawn in fp32 and, for bf16, rounded to bf16 (nearest even).  ``N``
+    keeps the first N images."""
+    L = layer
+    rx, rd = (np.random.default_rng(s) for s in np.random.SeedSequence(L.seed).spawn(2))
+    n_keep = L.N if N is None else N
+    sd = 1.0 / np.sqrt(L.R * L.S * L.C)
+    x = rx.normal(0.0, sd, size=(L.N, L.H, L.W, L.C)).astype(np.float32)[:n_keep]
+    dy = rd.normal(0.0, 1.0, size=(L.N, L.Ho, L.Wo, L.K)).astype(np.float32)[:n_keep]
+    if L.dtype == "bf16":
+        x, dy = float_to_bf16_bits(x), float_to_bf16_bits(dy)
+    return WgradInputs(L, np.ascontiguousarray(x), np.ascontiguousarray(dy))
+
+
 def float_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """fp32 samples -> bf16 bit patterns (uint16), round to nearest even.
 
