@@ -87,6 +87,7 @@ struct WgArgs {
   int64_t lp;
   uint32_t x_bytes, dy_bytes;
   uint32_t hw_mul, hw_add, hw_shift, wo_mul, wo_add, wo_shift;
+  int32_t wo_ge_e;  // Wo >= pixels per gather group: one wrap at most
 };
 
 __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint32_t shift) {
@@ -159,17 +160,22 @@ __device__ inline void wg_transpose(const i32x4 (&v)[E], i32x4 (&o)[E]) {
 // VEC: C and K are multiples of E, so every gathered chunk is one 16-byte
 // load; otherwise elements are gathered one by one (any shape).
 //
-// Per stage (BM = 8*E pixels): every thread fetches its tasks' chunks (one
-// task = one 16-byte column chunk x E pixels of dy or of the patch matrix),
-// transposes them and writes them to the stage's LDS buffer; a barrier; the
-// four waves (a 2x2 or 1x4 grid over the tile) then run the stage's MFMAs
-// while the next stage's chunks are in flight.  Two LDS buffers alternate.
+// Per stage (BM = 8*E pixels) every thread fetches its tasks' chunks (one
+// task = one 16-byte column chunk x E consecutive pixels, of dy or of the
+// patch matrix), transposes them in registers and writes them to the stage's
+// LDS buffer; after one barrier the four waves (a 2x2 or 1x4 grid over the
+// tile) run the stage's MFMAs.  Loads run two stages ahead (two register
+// sets), LDS holds two stages.  The patch gather costs more VALU work than
+// the dy gather, so the two halves of the workgroup swap roles on odd
+// stages: every SIMD then carries the same load.
 template <int DT, int TK, bool VEC>
-__global__ __launch_bounds__(kWgThreads) void wgrad_kernel(WgArgs a) {
+__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void wgrad_kernel(WgArgs a) {
   constexpr int ES = DT == FCONV_BF16 ? 2 : 4;
   constexpr int E = 16 / ES;
   constexpr int BM = 8 * E;                  // pixels per stage
   constexpr int ROWS = TK + kWgTKK;          // LDS rows per stage
+  constexpr int STAGE_BYTES = ROWS * kWgRowBytes;
   constexpr int NT_DY = (TK / E) * 8;        // dy tasks per stage
   constexpr int NT = NT_DY + (kWgTKK / E) * 8;
   constexpr int TPT = (NT + kWgThreads - 1) / kWgThreads;  // tasks per thread
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kWgThreads) void wgrad_kernel(WgArgs a) {
   constexpr int NI = 4;                      // 16-row MFMA tiles per wave along k
   constexpr int NJ = kWgTKK / WKK / 16;      // along kk (2 or 4)
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][ROWS * kWgRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
 
   // Block -> (pixel range, tile).  Consecutive logical ids share a pixel
   // range; the remap puts consecutive ids on one XCD when the grid is a
@@ -204,118 +210,190 @@ __global__ __launch_bounds__(kWgThreads) void wgrad_kernel(WgArgs a) {
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
 
-  // Per-task constants (a thread's tasks keep their column chunk across
-  // stages; only the pixels move).
-  int t_isdy[TPT], t_cc[TPT], t_pc[TPT], t_col[TPT], t_r[TPT], t_s[TPT], t_c[TPT];
-  bool t_on[TPT];
+  // Task constants of both roles (role p: task id (tid ^ 128p) + 256 i; the
+  // xor swaps waves 0,1 with 2,3 and keeps every wave's tasks of one kind,
+  // since the task counts are multiples of 64).
+  struct Task {
+    int on, isdy;   // wave-uniform
+    int pm;         // first pixel of the task inside the stage (E * group)
+    int col;        // first channel k (dy) or column kk (patch) of the chunk
+    int dr, ds, c;  // patch: tap row/col offsets r - pt, s - pl and channel
+    int laddr;      // LDS byte offset of the chunk's first row, | slot xor << 4
+  };
+  Task tk[2][TPT];
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    const int t = tid + i * kWgThreads;
-    t_on[i] = t < NT;
-    const bool isdy = t < NT_DY;
-    const int local = isdy ? t : t - NT_DY;
-    const int ncc = (isdy ? TK : kWgTKK) / E;
-    t_isdy[i] = isdy;
-    t_cc[i] = local % ncc;
-    t_pc[i] = local / ncc;
-    t_col[i] = (isdy ? k0 : kk0) + t_cc[i] * E;  // first channel k / column kk
-    t_r[i] = t_s[i] = t_c[i] = 0;
-    if (!isdy && VEC) {
-      const int rs = t_col[i] / a.C;
-      t_c[i] = t_col[i] - rs * a.C;
-      t_r[i] = rs / a.S;
-      t_s[i] = rs - t_r[i] * a.S;
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int t = (tid ^ (p ? 128 : 0)) + i * kWgThreads;
+      Task& T = tk[p][i];
+      T.on = t < NT;
+      T.isdy = t < NT_DY;
+      const int local = T.isdy ? t : t - NT_DY;
+      const int ncc = (T.isdy ? TK : kWgTKK) / E;
+      const int cc = local % ncc;
+      const int pc = local / ncc;
+      T.pm = pc * E;
+      T.col = (T.isdy ? k0 : kk0) + cc * E;
+      T.dr = T.ds = T.c = 0;
+      if (!T.isdy && VEC) {
+        const int rs = T.col / a.C;
+        T.c = T.col - rs * a.C;
+        const int r = rs / a.S;
+        T.dr = r - a.pt;
+        T.ds = rs - r * a.S - a.pl;
+      }
+      // Row of channel j of the chunk: row0 + j.  With row0 a multiple of E
+      // (E = 4 or 8) the slot of pixel group pc in that row is
+      // (pc ^ s0) ^ j, s0 the xor of row0 (see wg_slot); row0 * 128 has
+      // bits 4..6 clear, so the slot bits can ride in those.
+      const int row0 = (T.isdy ? 0 : TK) + cc * E;
+      T.laddr = row0 * kWgRowBytes + ((pc ^ ((row0 ^ (row0 >> 3)) & 7)) << 4);
     }
   }
 
-  // Element offset of input pixel (n, ho*sh - pt + r, wo*sw - pl + s), or -1
-  // outside the image / past the pixel range.
-  auto patch_pixel = [&](int m, int r, int s) -> int64_t {
+  // Element offset (in x) of the patch value of pixel m at tap (dr, ds),
+  // channel c; -1 outside the image or past the pixel range.  Used by the
+  // element-wise gather only.
+  auto patch_elem = [&](int m, int dr, int ds, int c) -> int64_t {
     if (m >= m_end) return -1;
     const uint32_t n = fast_div(static_cast<uint32_t>(m), a.hw_mul, a.hw_add, a.hw_shift);
     const uint32_t rem = static_cast<uint32_t>(m) - n * static_cast<uint32_t>(a.Ho * a.Wo);
     const uint32_t ho = fast_div(rem, a.wo_mul, a.wo_add, a.wo_shift);
     const uint32_t wo = rem - ho * static_cast<uint32_t>(a.Wo);
-    const int hi = static_cast<int>(ho) * a.sh - a.pt + r;
-    const int wi = static_cast<int>(wo) * a.sw - a.pl + s;
+    const int hi = static_cast<int>(ho) * a.sh + dr;
+    const int wi = static_cast<int>(wo) * a.sw + ds;
     if (hi < 0 || hi >= a.H || wi < 0 || wi >= a.W) return -1;
-    return ((static_cast<int64_t>(n) * a.H + hi) * a.W + wi);
+    return ((static_cast<int64_t>(n) * a.H + hi) * a.W + wi) * a.C + c;
   };
 
-  i32x4 reg[TPT][E];
-  auto fetch = [&](int st) {
+  auto fetch = [&](int st, const Task (&tasks)[TPT], i32x4 (&R)[TPT][E]) {
     const int mb = m_begin + st * BM;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
+      const Task& T = tasks[i];
+      int m0 = mb + T.pm;
+      // Opaque per stage: otherwise every pixel's offset becomes an
+      // induction variable of the stage loop, and they do not fit in
+      // registers.
+      asm volatile("" : "+v"(m0));
+      if constexpr (VEC) {
+        uint32_t off[E];
+        if (__builtin_amdgcn_readfirstlane(T.isdy)) {
+          // dy rows are contiguous: pixel m0 + e at (m0 + e) * K + col.
+          const bool ok = T.on && T.col < a.K;
+          const uint32_t o0 = static_cast<uint32_t>((m0 * a.K + T.col) * ES);
+          const uint32_t step = static_cast<uint32_t>(a.K * ES);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int m = mb + t_pc[i] * E + e;
-        if constexpr (VEC) {
-          uint32_t off = kOutOfRange;
-          if (t_on[i]) {
-            if (t_isdy[i]) {
-              if (m < m_end && t_col[i] < a.K)
-                off = static_cast<uint32_t>((static_cast<int64_t>(m) * a.K + t_col[i]) * ES);
-            } else if (t_col[i] < a.Kg) {
-              const int64_t px = patch_pixel(m, t_r[i], t_s[i]);
-              if (px >= 0) off = static_cast<uint32_t>((px * a.C + t_c[i]) * ES);
-            }
-          }
-          // Every wave's tasks are all dy or all patch (the task counts are
-          // multiples of 64), so the descriptor choice is wave-uniform.
-          const bool dy_task = __builtin_amdgcn_readfirstlane(t_isdy[i]) != 0;
-          reg[i][e] = __builtin_amdgcn_raw_buffer_load_b128(dy_task ? dr : xr, off, 0, 0);
+          for (int e = 0; e < E; ++e)
+            off[e] = (ok && m0 + e < m_end) ? o0 + e * step : kOutOfRange;
         } else {
-          // Element by element: column j of the chunk is channel / column
-          // t_col + j, each with its own bounds (and tap for the patch).
+          const bool ok = T.on && T.col < a.Kg;
+          // Decode the group's first pixel once; the others follow by
+          // stepping wo (at most one wrap while Wo >= E).
+          const uint32_t um0 = static_cast<uint32_t>(m0);
+          const uint32_t n0 = fast_div(um0, a.hw_mul, a.hw_add, a.hw_shift);
+          const uint32_t rem = um0 - n0 * static_cast<uint32_t>(a.Ho * a.Wo);
+          const uint32_t ho0 = fast_div(rem, a.wo_mul, a.wo_add, a.wo_shift);
+          const int wo0 = static_cast<int>(rem - ho0 * static_cast<uint32_t>(a.Wo));
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            int n = static_cast<int>(n0), ho = static_cast<int>(ho0), wo = wo0 + e;
+            if (a.wo_ge_e) {
+              const bool c1 = wo >= a.Wo;
+              wo = c1 ? wo - a.Wo : wo;
+              ho = ho + (c1 ? 1 : 0);
+              const bool c2 = ho >= a.Ho;
+              ho = c2 ? 0 : ho;
+              n = n + (c2 ? 1 : 0);
+            } else {
+              const uint32_t um = um0 + e;
+              const uint32_t nn = fast_div(um, a.hw_mul, a.hw_add, a.hw_shift);
+              const uint32_t rr = um - nn * static_cast<uint32_t>(a.Ho * a.Wo);
+              const uint32_t hh = fast_div(rr, a.wo_mul, a.wo_add, a.wo_shift);
+              n = static_cast<int>(nn);
+              ho = static_cast<int>(hh);
+              wo = static_cast<int>(rr - hh * static_cast<uint32_t>(a.Wo));
+            }
+            const int hi = ho * a.sh + T.dr;
+            const int wi = wo * a.sw + T.ds;
+            const bool in = ok && m0 + e < m_end && static_cast<uint32_t>(hi) < static_cast<uint32_t>(a.H) &&
+                            static_cast<uint32_t>(wi) < static_cast<uint32_t>(a.W);
+            off[e] = in ? static_cast<uint32_t>((((n * a.H + hi) * a.W + wi) * a.C + T.c) * ES)
+                        : kOutOfRange;
+          }
+        }
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_readfirstlane(T.isdy) ? dr : xr;
+#pragma unroll
+        for (int e = 0; e < E; ++e) R[i][e] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[e], 0, 0);
+      } else {
+        // Element by element: column j of the chunk is channel / column
+        // col + j, each with its own bounds (and tap for the patch).
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int m = m0 + e;
           union {
             i32x4 v;
             uint16_t h[8];
             float f[4];
           } u;
           u.v = i32x4{0, 0, 0, 0};
-          if (t_on[i] && m < m_end) {
+          if (T.on && m < m_end) {
 #pragma unroll
             for (int j = 0; j < E; ++j) {
-              const int col = t_col[i] + j;
+              const int col = T.col + j;
               int64_t idx = -1;
-              if (t_isdy[i]) {
+              if (T.isdy) {
                 if (col < a.K) idx = static_cast<int64_t>(m) * a.K + col;
               } else if (col < a.Kg) {
                 const int rs = col / a.C;
-                const int c = col - rs * a.C;
                 const int r = rs / a.S;
-                const int64_t px = patch_pixel(m, r, rs - r * a.S);
-                if (px >= 0) idx = px * a.C + c;
+                idx = patch_elem(m, r - a.pt, rs - r * a.S - a.pl, col - rs * a.C);
               }
               if (idx >= 0) {
                 if constexpr (DT == FCONV_BF16)
-                  u.h[j] = (t_isdy[i] ? static_cast<const uint16_t*>(a.dy)
-                                      : static_cast<const uint16_t*>(a.x))[idx];
+                  u.h[j] = (T.isdy ? static_cast<const uint16_t*>(a.dy)
+                                   : static_cast<const uint16_t*>(a.x))[idx];
                 else
-                  u.f[j] = (t_isdy[i] ? static_cast<const float*>(a.dy)
-                                      : static_cast<const float*>(a.x))[idx];
+                  u.f[j] = (T.isdy ? static_cast<const float*>(a.dy)
+                                   : static_cast<const float*>(a.x))[idx];
               }
             }
           }
-          reg[i][e] = u.v;
+          R[i][e] = u.v;
         }
       }
     }
   };
 
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const Task (&tasks)[TPT], const i32x4 (&R)[TPT][E]) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      if (!t_on[i]) continue;
-      i32x4 o[E];
-      wg_transpose<DT, E>(reg[i], o);
-      const int row0 = (t_isdy[i] ? 0 : TK) + t_cc[i] * E;
+      const Task& T = tasks[i];
+      if (!T.on) continue;
+      uint8_t* base = lds + buf * STAGE_BYTES;
+      // Opaque copy: keeps the compiler from hoisting the E row addresses
+      // of every task and buffer out of the stage loop (they would not fit
+      // in registers); each costs one xor per stage here.
+      int la = T.laddr;
+      asm volatile("" : "+v"(la));
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        const int row = row0 + j;
-        *reinterpret_cast<i32x4*>(&lds[buf][row * kWgRowBytes + wg_slot(row, t_pc[i]) * 16]) =
-            o[j];
+        // Channel j of the chunk for the E pixels: the transposed block's
+        // row j (pixel e at element e).
+        i32x4 o;
+        if constexpr (DT == FCONV_BF16) {
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            o[d] = static_cast<int32_t>(__builtin_amdgcn_perm(
+                static_cast<uint32_t>(R[i][2 * d + 1][j >> 1]),
+                static_cast<uint32_t>(R[i][2 * d][j >> 1]), sel));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = R[i][e][j];
+        }
+        *reinterpret_cast<i32x4*>(base + j * kWgRowBytes + (la ^ (j << 4))) = o;
       }
     }
   };
@@ -326,38 +404,55 @@ __global__ __launch_bounds__(kWgThreads) void wgrad_kernel(WgArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int arow0 = wk * 64 + (lane & 15);
-  const int brow0 = TK + wkk * (NJ * 16) + (lane & 15);
+  // Fragment addresses (stage-relative) of k-step 0, fixed for the whole
+  // loop: row r reads pixel group g at slot g ^ f(r).  K-step 1 reads group
+  // 4 + g, whose slot differs in bit 2: the address xor 64.
   const int g = lane >> 4;
+  int aaddr[NI], baddr[NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = wk * 64 + 16 * i + (lane & 15);
+    aaddr[i] = row * kWgRowBytes + wg_slot(row, g) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = TK + wkk * (NJ * 16) + 16 * j + (lane & 15);
+    baddr[j] = row * kWgRowBytes + wg_slot(row, g) * 16;
+  }
 
-  if (nst > 0) fetch(0);
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    stash(buf);
-    if (st + 1 < nst) fetch(st + 1);
-    __syncthreads();
-    // Two k-steps per stage: k-step q reads pixel runs 4q .. 4q+3.
+  auto compute = [&](int buf) {
+    const uint8_t* base = lds + buf * STAGE_BYTES;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int chunk = 4 * q + g;
-      i32x4 af[NI], bfr[NJ];
+      i32x4 bfr[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        bfr[j] = *reinterpret_cast<const i32x4*>(base + (baddr[j] ^ (q << 6)));
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int row = arow0 + 16 * i;
-        af[i] = *reinterpret_cast<const i32x4*>(
-            &lds[buf][row * kWgRowBytes + wg_slot(row, chunk) * 16]);
+        const i32x4 af = *reinterpret_cast<const i32x4*>(base + (aaddr[i] ^ (q << 6)));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = wg_mma<DT>(af, bfr[j], acc[i][j]);
       }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = brow0 + 16 * j;
-        bfr[j] = *reinterpret_cast<const i32x4*>(
-            &lds[buf][row * kWgRowBytes + wg_slot(row, chunk) * 16]);
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = wg_mma<DT>(af[i], bfr[j], acc[i][j]);
     }
+  };
+
+  // Even stages use role 0, register set R0 and LDS buffer 0; odd stages
+  // role 1, R1 and buffer 1.  Stage st's registers are refilled with stage
+  // st + 2 right after they are written to LDS.
+  i32x4 R0[TPT][E], R1[TPT][E];
+  if (nst > 0) fetch(0, tk[0], R0);
+  if (nst > 1) fetch(1, tk[1], R1);
+  for (int st = 0; st < nst; st += 2) {
+    stash(0, tk[0], R0);
+    if (st + 2 < nst) fetch(st + 2, tk[0], R0);
+    __syncthreads();
+    compute(0);
+    if (st + 1 >= nst) break;
+    stash(1, tk[1], R1);
+    if (st + 3 < nst) fetch(st + 3, tk[1], R1);
+    __syncthreads();
+    compute(1);
   }
 
   // Lane holds D[k][kk] for k = kbase + 4g + t (t = 0..3), kk = kkbase + lane%16.
@@ -614,6 +709,7 @@ fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan p, void* stream, const void* 
   a.dy_bytes = static_cast<uint32_t>(db);
   a.hw_mul = p->hw_div.mul; a.hw_add = p->hw_div.add; a.hw_shift = p->hw_div.shift;
   a.wo_mul = p->wo_div.mul; a.wo_add = p->wo_div.add; a.wo_shift = p->wo_div.shift;
+  a.wo_ge_e = p->Wo >= p->E;
   hipError_t e = p->d.dtype == FCONV_BF16 ? launch_wgrad_dt<FCONV_BF16>(p, a, s)
                                            : launch_wgrad_dt<FCONV_FP32>(p, a, s);
   if (e != hipSuccess) return FCONV_ERR_DEVICE;
