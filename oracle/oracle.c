@@ -369,11 +369,6 @@ void oracle_epilogue_i8(const int32_t* acc, long M, int K, float conv_input_scal
 }
 
 /*
- * Float epilogue: bias, then batch-norm inference, then ReLU, each optional,
- * in that order, in double.  bias == NULL skips the bias; gamma == NULL skips
- * the batch norm (then beta/mean/var are ignored).
- */
-/*
  * Weight gradient, in double: x [N][H][W][C], dy [N][Ho][Wo][K] (both as
  * double), dw [R][S][C][K].  d as for the convolutions.
  */
@@ -405,6 +400,11 @@ int oracle_wgrad_direct(const double* x, const double* dy, const int* d, double*
   return ORACLE_OK;
 }
 
+/*
+ * Float epilogue: bias, then batch-norm inference, then ReLU, each optional,
+ * in that order, in double.  bias == NULL skips the bias; gamma == NULL skips
+ * the batch norm (then beta/mean/var are ignored).
+ */
 /* Activation modes of the float epilogue. */
 #define ORACLE_ACT_NONE 0
 #define ORACLE_ACT_RELU 1
