@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <limits.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -50,6 +51,7 @@ struct fconv_wgrad_plan_s {
   int32_t Kg;        // R*S*C
   bool out_fp32;     // dw written as fp32
   bool vec;          // C % E == 0 and K % E == 0: 16-byte gathers
+  bool dma;          // vec shapes: the direct-to-LDS kernel (else register-staged)
   int32_t tk;        // output channels per tile (64 or 128)
   int32_t tiles_k, tiles_kk;
   int32_t splits;    // pixel ranges
@@ -153,6 +155,51 @@ __device__ inline void wg_transpose(const i32x4 (&v)[E], i32x4 (&o)[E]) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[j][e] = v[e][j];
+  }
+}
+
+// Store a wave's accumulators: lane holds D[k][kk] for k = k0 + 64 wk +
+// 16 i + 4 g + t (t = 0..3) and kk = kk0 + wkk * 16 NJ + 16 j + lane % 16; to
+// the pixel range's partial tile (fp32) or straight to dw (fp32 or bf16).
+template <int NI, int NJ>
+__device__ inline void wg_store(const WgArgs& a, const f32x4 (&acc)[NI][NJ], int split, int k0,
+                                int kk0, int wk, int wkk, int lane) {
+  const int g = lane >> 4;
+  const bool kvec4 = (a.K & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int k = k0 + wk * 64 + 16 * i + 4 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kk = kk0 + wkk * (NJ * 16) + 16 * j + (lane & 15);
+      if (kk >= a.Kg || k >= a.K) continue;
+      const f32x4 v = acc[i][j];
+      const int64_t base = static_cast<int64_t>(kk) * a.K + k;
+      if (a.out_mode == 0) {
+        float* o = static_cast<float*>(a.out) + split * a.lp + base;
+        if (kvec4) {
+          *reinterpret_cast<f32x4*>(o) = v;
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
+        }
+      } else if (a.out_mode == 1) {
+        float* o = static_cast<float*>(a.out) + base;
+        if (kvec4) {
+          *reinterpret_cast<f32x4*>(o) = v;
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
+        }
+      } else {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + base;
+        if (kvec4) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+          *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+        } else {
+          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = f32_to_bf16_rne(v[t]);
+        }
+      }
+    }
   }
 }
 
@@ -455,43 +502,276 @@ void wgrad_kernel(WgArgs a) {
     compute(1);
   }
 
-  // Lane holds D[k][kk] for k = kbase + 4g + t (t = 0..3), kk = kkbase + lane%16.
-  const bool kvec4 = (a.K & 3) == 0;
+  wg_store<NI, NJ>(a, acc, split, k0, kk0, wk, wkk, lane);
+}
+
+// ------------------------------------------------ direct-to-LDS kernel
+//
+// For C and K multiples of the 16-byte chunk.  Both operands are copied into
+// LDS in their natural, pixel-major layout by buffer->LDS copies (no
+// registers, no transposes): a stage holds BM pixel rows of dy (TK channels)
+// followed by BM pixel rows of the patch matrix (128 columns).  Each 16-byte
+// slot s of pixel row p is stored at slot s ^ swz(p).
+//
+// Fragments.  bf16: the gfx950 transposed LDS read (ds_read_b64_tr_b16)
+// works on 16-lane groups: lane i's element e is element i % 4 of the
+// 64-bit chunk addressed by lane 4e + i / 4 of its group (measured on the
+// device).  Lane (j, g) (j = lane % 16, g = lane / 16) therefore addresses
+// pixel row 8g + 4h + j / 4, columns c0 + 4 (j % 4) .. +3, and receives column
+// c0 + j at pixels 8g + 4h .. +3: two reads (h = 0, 1) give the 8-pixel
+// MFMA fragment of column c0 + j, for both operands alike.  fp32: one
+// element per lane per 16x16x4 MFMA, read as is (pixel 4 kstep + g,
+// column c0 + j).
+//
+// Swizzles.  bf16: one transposed read touches pixel rows 8g + 4h + (0..3)
+// of the 4 groups, 32 bytes each; swz(p) = 2 (p & 3) + 8 ((p >> 3) & 1) puts
+// them on 8 distinct 32-byte bank groups, twice over, the minimum for 512
+// bytes.  fp32: a read touches 4 rows, 64 bytes each; swz(p) = 4 (p & 3)
+// separates them.
+//
+// Pipeline (as the forward tiled kernel): four LDS stage buffers, each its
+// own __shared__ array; copies run three stages ahead; a step waits for its
+// own copies of the stage, meets the other waves at a plain barrier, issues
+// the copies three stages ahead into the buffer of the stage before, reads
+// the stage's fragments and runs its MFMAs.
+template <int DT, int TK>
+struct DmaCfg {
+  static constexpr int ES = DT == FCONV_BF16 ? 2 : 4;
+  static constexpr int BM = DT == FCONV_BF16 ? 32 : 16;  // pixels per stage
+  static constexpr int RB_DY = TK * ES;                  // bytes per dy row
+  static constexpr int RB_P = kWgTKK * ES;               // bytes per patch row
+  static constexpr int DY_BYTES = BM * RB_DY;
+  static constexpr int SB = DY_BYTES + BM * RB_P;        // stage bytes
+  static constexpr int NC = SB / 1024;                   // 1 KiB copies per stage
+  static constexpr int NCW = NC / 4;                     // per wave
+  static_assert(SB % 4096 == 0, "stage must split into 4 waves of 1 KiB copies");
+  static_assert(DY_BYTES % 1024 == 0, "dy rows must fill whole copies");
+};
+
+// Slot xor of pixel row p in a row of RB bytes (RB / 16 slots; the xor
+// stays inside the row: 128-byte rows drop the bit-3 term).
+template <int DT, int RB>
+__device__ inline int dma_swz(int p) {
+  if constexpr (DT == FCONV_BF16) return (((p & 3) << 1) | (((p >> 3) & 1) << 3)) & (RB / 16 - 1);
+  return ((p & 3) << 2) & (RB / 16 - 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_t;
+typedef __attribute__((address_space(3))) float* lds_f32_t;
+
+template <int DT, int TK>
+__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void wgrad_dma_kernel(WgArgs a) {
+  using Cfg = DmaCfg<DT, TK>;
+  constexpr int ES = Cfg::ES, BM = Cfg::BM, NCW = Cfg::NCW;
+  constexpr int E = 16 / ES;
+  constexpr int WK = TK / 64;
+  constexpr int WKK = 4 / WK;
+  constexpr int NI = 4;
+  constexpr int NJ = kWgTKK / WKK / 16;
+  __shared__ __attribute__((aligned(1024))) char buf0[Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf1[Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf2[Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf3[Cfg::SB];
+
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  if (logical >= a.blocks) return;
+  const int tiles = a.tiles_k * a.tiles_kk;
+  const int split = logical / tiles;
+  const int tile = logical % tiles;
+  const int k0 = (tile % a.tiles_k) * TK;
+  const int kk0 = (tile / a.tiles_k) * kWgTKK;
+  const int m_begin = split * a.m_per_split;
+  const int m_end = min(a.M, m_begin + a.m_per_split);
+  const int nst = (m_end - m_begin + BM - 1) / BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wk = wave % WK, wkk = wave / WK;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
+
+  // This wave's copies: q = wave + 4 i.  Lane l of copy q fills stage bytes
+  // q * 1024 + 16 l: pixel row p and stored slot s' there, i.e. the chunk
+  // s = s' ^ swz(p) of that row.
+  int c_p[NCW], c_col[NCW], c_dr[NCW], c_ds[NCW], c_c[NCW];
+  bool c_ok[NCW];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int k = k0 + wk * 64 + 16 * i + 4 * g;
+  for (int i = 0; i < NCW; ++i) {
+    const int q = wave + 4 * i;
+    const int byte = q * 1024 + lane * 16;
+    const bool isdy = q * 1024 < Cfg::DY_BYTES;  // wave-uniform
+    const int rb = isdy ? Cfg::RB_DY : Cfg::RB_P;
+    const int rel = isdy ? byte : byte - Cfg::DY_BYTES;
+    const int p = rel / rb;
+    const int s = ((rel % rb) / 16) ^ (isdy ? dma_swz<DT, Cfg::RB_DY>(p) : dma_swz<DT, Cfg::RB_P>(p));
+    c_p[i] = p;
+    c_col[i] = (isdy ? k0 : kk0) + s * E;
+    c_dr[i] = c_ds[i] = c_c[i] = 0;
+    if (isdy) {
+      c_ok[i] = c_col[i] < a.K;
+    } else {
+      c_ok[i] = c_col[i] < a.Kg;
+      const int rs = c_col[i] / a.C;
+      c_c[i] = c_col[i] - rs * a.C;
+      const int r = rs / a.S;
+      c_dr[i] = r - a.pt;
+      c_ds[i] = rs - r * a.S - a.pl;
+    }
+  }
+
+  int nx_st = 0;
+  auto issue = [&](char* buf) __attribute__((always_inline)) {
+    const int st = nx_st++;
+    const int mb = m_begin + st * BM;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+      const int q = wave + 4 * i;
+      const int m = mb + c_p[i];
+      const bool live = c_ok[i] && st < nst && m < m_end;
+      uint32_t off = kOutOfRange;
+      if (q * 1024 < Cfg::DY_BYTES) {
+        if (live) off = static_cast<uint32_t>((m * a.K + c_col[i]) * ES);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_ptr_t)(buf + q * 1024), 16, off, 0, 0, 0);
+      } else {
+        const uint32_t um = static_cast<uint32_t>(live ? m : 0);
+        const uint32_t n = fast_div(um, a.hw_mul, a.hw_add, a.hw_shift);
+        const uint32_t rem = um - n * static_cast<uint32_t>(a.Ho * a.Wo);
+        const uint32_t ho = fast_div(rem, a.wo_mul, a.wo_add, a.wo_shift);
+        const int wo = static_cast<int>(rem - ho * static_cast<uint32_t>(a.Wo));
+        const int hi = static_cast<int>(ho) * a.sh + c_dr[i];
+        const int wi = wo * a.sw + c_ds[i];
+        if (live && static_cast<uint32_t>(hi) < static_cast<uint32_t>(a.H) &&
+            static_cast<uint32_t>(wi) < static_cast<uint32_t>(a.W))
+          off = static_cast<uint32_t>(
+              (((static_cast<int>(n) * a.H + hi) * a.W + wi) * a.C + c_c[i]) * ES);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + q * 1024), 16, off, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x4 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int j16 = lane & 15, g = lane >> 4;
+  // Fragment addresses, stage-relative.
+  constexpr int NH = DT == FCONV_BF16 ? 2 : 4;  // bf16: two tr reads; fp32: 4 k-steps
+  int aaddr[NH][NI], baddr[NH][NJ];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int col = wk * 64 + 16 * i;
+      if constexpr (DT == FCONV_BF16) {
+        const int p = 8 * g + 4 * h + (j16 >> 2);
+        const int cb = (col + 4 * (j16 & 3)) * 2;  // byte in row
+        aaddr[h][i] = p * Cfg::RB_DY + (((cb >> 4) ^ dma_swz<DT, Cfg::RB_DY>(p)) << 4) + (cb & 15);
+      } else {
+        const int p = 4 * h + g;
+        const int cb = (col + j16) * 4;
+        aaddr[h][i] = p * Cfg::RB_DY + (((cb >> 4) ^ dma_swz<DT, Cfg::RB_DY>(p)) << 4) + (cb & 15);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int kk = kk0 + wkk * (NJ * 16) + 16 * j + (lane & 15);
-      if (kk >= a.Kg || k >= a.K) continue;
-      const f32x4 v = acc[i][j];
-      const int64_t base = static_cast<int64_t>(kk) * a.K + k;
-      if (a.out_mode == 0) {
-        float* o = static_cast<float*>(a.out) + split * a.lp + base;
-        if (kvec4) {
-          *reinterpret_cast<f32x4*>(o) = v;
-        } else {
-          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
-        }
-      } else if (a.out_mode == 1) {
-        float* o = static_cast<float*>(a.out) + base;
-        if (kvec4) {
-          *reinterpret_cast<f32x4*>(o) = v;
-        } else {
-          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = v[t];
-        }
+      const int col = wkk * (NJ * 16) + 16 * j;
+      if constexpr (DT == FCONV_BF16) {
+        const int p = 8 * g + 4 * h + (j16 >> 2);
+        const int cb = (col + 4 * (j16 & 3)) * 2;
+        baddr[h][j] = Cfg::DY_BYTES + p * Cfg::RB_P + (((cb >> 4) ^ dma_swz<DT, Cfg::RB_P>(p)) << 4) + (cb & 15);
       } else {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + base;
-        if (kvec4) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
-          *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-        } else {
-          for (int t = 0; t < 4 && k + t < a.K; ++t) o[t] = f32_to_bf16_rne(v[t]);
-        }
+        const int p = 4 * h + g;
+        const int cb = (col + j16) * 4;
+        baddr[h][j] = Cfg::DY_BYTES + p * Cfg::RB_P + (((cb >> 4) ^ dma_swz<DT, Cfg::RB_P>(p)) << 4) + (cb & 15);
       }
     }
   }
+
+  auto mma_stage = [&](const char* buf) __attribute__((always_inline)) {
+    if constexpr (DT == FCONV_BF16) {
+      v4i16 al[NI][2], bl[NJ][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          al[i][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(buf + aaddr[h][i]));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          bl[j][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(buf + baddr[h][j]));
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bf16x8 af = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(al[i][0], al[i][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x8 bf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(bl[j][0], bl[j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[i][j], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        float al[NI], bl[NJ];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) al[i] = *(lds_f32_t)(buf + aaddr[h][i]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bl[j] = *(lds_f32_t)(buf + baddr[h][j]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(al[i], bl[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Own copies of the stage landed: the two later stages' (2 NCW) may
+  // still be in flight.
+  auto wait_stage = [&]() {
+    if constexpr (NCW == 4) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0f76);                     // vmcnt(6)
+  };
+  auto step = [&](const char* cur, char* next3) __attribute__((always_inline)) {
+    wait_stage();
+    barrier();
+    issue(next3);
+    mma_stage(cur);
+    // The MFMAs (and so the LDS reads they consume) stay ahead of the next
+    // step's barrier, after which another wave's copies reuse this buffer.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(buf0);
+  issue(buf1);
+  issue(buf2);
+  int st = 0;
+  for (; st + 4 <= nst; st += 4) {
+    step(buf0, buf3);
+    step(buf1, buf0);
+    step(buf2, buf1);
+    step(buf3, buf2);
+  }
+  if (st < nst) step(buf0, buf3);
+  if (st + 1 < nst) step(buf1, buf0);
+  if (st + 2 < nst) step(buf2, buf1);
+  __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
+
+  wg_store<NI, NJ>(a, acc, split, k0, kk0, wk, wkk, lane);
 }
 
 // dw[i] = sum over pixel ranges z of part[z][i], in a fixed association
@@ -548,8 +828,17 @@ hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DT, int TK>
+hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
+  const int grid = (a.blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK>), dim3(grid), dim3(kWgThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
+  if (p->dma)
+    return p->tk == 128 ? launch_wgrad_dma<DT, 128>(a, s) : launch_wgrad_dma<DT, 64>(a, s);
   if (p->tk == 128)
     return p->vec ? launch_wgrad_main<DT, 128, true>(a, s) : launch_wgrad_main<DT, 128, false>(a, s);
   return p->vec ? launch_wgrad_main<DT, 64, true>(a, s) : launch_wgrad_main<DT, 64, false>(a, s);
@@ -563,7 +852,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
-const char* wgrad_kernel_name(int dtype, int tk, bool vec) {
+const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma) {
+  if (dma) {
+    if (dtype == FCONV_BF16) return tk == 128 ? "wgrad_dma_bf16_128" : "wgrad_dma_bf16_64";
+    return tk == 128 ? "wgrad_dma_f32_128" : "wgrad_dma_f32_64";
+  }
   if (dtype == FCONV_BF16)
     return tk == 128 ? (vec ? "wgrad_bf16_128" : "wgrad_bf16_128_elem")
                      : (vec ? "wgrad_bf16_64" : "wgrad_bf16_64_elem");
@@ -638,7 +931,11 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->ws_bytes = splits > 1 ? static_cast<size_t>(splits * p->lp * 4) : 0;
   p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
-  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec);
+  // FCONV_WGRAD_KERNEL=staged (environment) pins the register-staged
+  // kernel on shapes the direct-to-LDS kernel takes, for A/B comparisons.
+  const char* force = getenv("FCONV_WGRAD_KERNEL");
+  p->dma = p->vec && !(force && strcmp(force, "staged") == 0);
+  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma);
   *out = p;
   return FCONV_OK;
 }

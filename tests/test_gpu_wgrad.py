@@ -56,12 +56,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", ["default", "staged"])
 @pytest.mark.parametrize("out_fp32", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", CASES)
-def test_wgrad_small_shapes(case, dtype, out_fp32):
+def test_wgrad_small_shapes(case, dtype, out_fp32, kernel, monkeypatch):
+    """Both kernels: the default (direct-to-LDS where C and K fill 16-byte
+    chunks) and the register-staged one (FCONV_WGRAD_KERNEL=staged)."""
     if dtype == "fp32" and out_fp32:
         pytest.skip("fp32 plans always write fp32")
+    if kernel == "staged":
+        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
     N, H, W, C, K, R, S, stride, padding = case
     dev = device()
     plan = fc.WgradPlan(N, H, W, C, K, R, S, stride, padding, dtype, out_fp32=out_fp32)
@@ -107,9 +112,12 @@ def test_wgrad_is_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("kernel", ["default", "staged"])
 @pytest.mark.parametrize("name", list(wl.WGRAD_LAYERS))
-def test_wgrad_full_workload(name):
+def test_wgrad_full_workload(name, kernel, monkeypatch):
     """The full benchmark workloads, every element against the oracle."""
+    if kernel == "staged":
+        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
     dev = device()
     L = wl.WGRAD_LAYERS[name]
     inp = wl.make_wgrad_inputs(L)
