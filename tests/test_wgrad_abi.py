@@ -80,7 +80,7 @@ def test_workloads_and_workspace():
         kg_k = L.R * L.S * L.C * L.K
         # partial sums: a whole number of fp32 dW copies (or none)
         assert g.workspace_bytes % (4 * ((kg_k + 3) // 4)) == 0
-        assert g.kernel_name.startswith("wgrad_" + ("bf16" if L.dtype == "bf16" else "f32"))
+        assert g.kernel_name.startswith("wgrad_dma_" + ("bf16" if L.dtype == "bf16" else "f32"))
 
 
 def test_run_checks_arguments():
