@@ -52,6 +52,7 @@ struct fconv_wgrad_plan_s {
   bool out_fp32;     // dw written as fp32
   bool vec;          // C % E == 0 and K % E == 0: 16-byte gathers
   bool dma;          // vec shapes: the direct-to-LDS kernel (else register-staged)
+  int32_t ring;      // direct-to-LDS kernel: stages in its LDS ring (4 or 8)
   int32_t tk;        // output channels per tile (64 or 128)
   int32_t tiles_k, tiles_kk;
   int32_t splits;    // pixel ranges
@@ -73,7 +74,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kWgThreads = 256;   // 4 waves
 constexpr int kWgTKK = 128;       // (r,s,c) columns per tile
 constexpr int kWgRowBytes = 128;  // one LDS row: 8 slots of 16 bytes
-constexpr int kWgTargetBlocks = 512;  // about two workgroups per CU
+constexpr int kWgTargetBlocks = 512;  // two workgroups per CU (256 CUs)
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every extent: reads 0
 constexpr int kBufferDword3 = 0x00020000;      // raw buffer descriptor, gfx9 family
 
@@ -561,8 +562,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_t;
 typedef __attribute__((address_space(3))) float* lds_f32_t;
 
-template <int DT, int TK>
-__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// s_waitcnt immediate for vmcnt(n) alone (gfx9: vmcnt bits [3:0] and
+// [15:14]; expcnt and lgkmcnt at their maximum, i.e. not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int DT, int TK, int NBUF>
+__global__ __launch_bounds__(kWgThreads)
+__attribute__((amdgpu_waves_per_eu(NBUF == 8 ? 1 : 2, 2)))  // the 8-stage ring fills a CU's LDS
 void wgrad_dma_kernel(WgArgs a) {
   using Cfg = DmaCfg<DT, TK>;
   constexpr int ES = Cfg::ES, BM = Cfg::BM, NCW = Cfg::NCW;
@@ -571,10 +577,17 @@ void wgrad_dma_kernel(WgArgs a) {
   constexpr int WKK = 4 / WK;
   constexpr int NI = 4;
   constexpr int NJ = kWgTKK / WKK / 16;
+  static_assert(NBUF == 4 || NBUF == 8, "ring of 4 or 8 stages");
+  constexpr int SB_HI = NBUF > 4 ? Cfg::SB : 16;
   __shared__ __attribute__((aligned(1024))) char buf0[Cfg::SB];
   __shared__ __attribute__((aligned(1024))) char buf1[Cfg::SB];
   __shared__ __attribute__((aligned(1024))) char buf2[Cfg::SB];
   __shared__ __attribute__((aligned(1024))) char buf3[Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf4[SB_HI];
+  __shared__ __attribute__((aligned(1024))) char buf5[SB_HI];
+  __shared__ __attribute__((aligned(1024))) char buf6[SB_HI];
+  __shared__ __attribute__((aligned(1024))) char buf7[SB_HI];
+  char* const bufs[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
 
   const int nb = gridDim.x;
   const int b = blockIdx.x;
@@ -740,35 +753,35 @@ void wgrad_dma_kernel(WgArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Own copies of the stage landed: the two later stages' (2 NCW) may
-  // still be in flight.
+  // Own copies of the stage landed: the NBUF - 2 later stages' may still be
+  // in flight.
   auto wait_stage = [&]() {
-    if constexpr (NCW == 4) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0f76);                     // vmcnt(6)
+    constexpr int imm = vmcnt_imm((NBUF - 2) * NCW);
+    __builtin_amdgcn_s_waitcnt(imm);
   };
-  auto step = [&](const char* cur, char* next3) __attribute__((always_inline)) {
+  auto step = [&](const char* cur, char* ahead) __attribute__((always_inline)) {
     wait_stage();
     barrier();
-    issue(next3);
+    issue(ahead);
     mma_stage(cur);
     // The MFMAs (and so the LDS reads they consume) stay ahead of the next
     // step's barrier, after which another wave's copies reuse this buffer.
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  issue(buf0);
-  issue(buf1);
-  issue(buf2);
+  // Stage st lives in buffer st % NBUF; step st copies stage st + NBUF - 1
+  // into the buffer of stage st - 1.  Whole trips of NBUF steps in the loop,
+  // the rest after it; past the last stage the copies are zeros.
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) issue(bufs[i]);
   int st = 0;
-  for (; st + 4 <= nst; st += 4) {
-    step(buf0, buf3);
-    step(buf1, buf0);
-    step(buf2, buf1);
-    step(buf3, buf2);
+  for (; st + NBUF <= nst; st += NBUF) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) step(bufs[i], bufs[(i + NBUF - 1) % NBUF]);
   }
-  if (st < nst) step(buf0, buf3);
-  if (st + 1 < nst) step(buf1, buf0);
-  if (st + 2 < nst) step(buf2, buf1);
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (st + i < nst) step(bufs[i], bufs[(i + NBUF - 1) % NBUF]);
   __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
   wg_store<NI, NJ>(a, acc, split, k0, kk0, wk, wkk, lane);
@@ -828,17 +841,19 @@ hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int TK>
+template <int DT, int TK, int NBUF>
 hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
   const int grid = (a.blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK>), dim3(grid), dim3(kWgThreads), 0, s, a);
+  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF>), dim3(grid), dim3(kWgThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
   if (p->dma)
-    return p->tk == 128 ? launch_wgrad_dma<DT, 128>(a, s) : launch_wgrad_dma<DT, 64>(a, s);
+    return p->ring == 8
+               ? (p->tk == 128 ? launch_wgrad_dma<DT, 128, 8>(a, s) : launch_wgrad_dma<DT, 64, 8>(a, s))
+               : (p->tk == 128 ? launch_wgrad_dma<DT, 128, 4>(a, s) : launch_wgrad_dma<DT, 64, 4>(a, s));
   if (p->tk == 128)
     return p->vec ? launch_wgrad_main<DT, 128, true>(a, s) : launch_wgrad_main<DT, 128, false>(a, s);
   return p->vec ? launch_wgrad_main<DT, 64, true>(a, s) : launch_wgrad_main<DT, 64, false>(a, s);
@@ -852,7 +867,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
-const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma) {
+const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring) {
+  if (dma && ring == 8) {
+    if (dtype == FCONV_BF16) return tk == 128 ? "wgrad_dma8_bf16_128" : "wgrad_dma8_bf16_64";
+    return tk == 128 ? "wgrad_dma8_f32_128" : "wgrad_dma8_f32_64";
+  }
   if (dma) {
     if (dtype == FCONV_BF16) return tk == 128 ? "wgrad_dma_bf16_128" : "wgrad_dma_bf16_64";
     return tk == 128 ? "wgrad_dma_f32_128" : "wgrad_dma_f32_64";
@@ -910,9 +929,24 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->tiles_kk = (p->Kg + kWgTKK - 1) / kWgTKK;
   const int64_t tiles = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
   const int64_t bm = 8 * p->E;
-  // Pixel ranges: enough workgroups for about two per CU, each range at
-  // least four stages long.
-  int64_t splits = (kWgTargetBlocks + tiles - 1) / tiles;
+  // FCONV_WGRAD_KERNEL=staged (environment) pins the register-staged
+  // kernel on shapes the direct-to-LDS kernel takes; FCONV_WGRAD_RING=4|8
+  // its LDS ring depth (both for A/B comparisons).
+  const char* force = getenv("FCONV_WGRAD_KERNEL");
+  p->dma = p->vec && !(force && strcmp(force, "staged") == 0);
+  // Ring depth: bf16 runs two workgroups per CU with 4-stage rings (the
+  // second workgroup's MFMAs fill the first one's waits: 40.5 us against 57
+  // with one 8-stage workgroup on the 28x28x256 layer); fp32, with 8x the
+  // MFMA time per byte, one workgroup with an 8-stage ring (180 us against
+  // 216).
+  const char* ring = getenv("FCONV_WGRAD_RING");
+  p->ring = d.dtype == FCONV_FP32 ? 8 : 4;
+  if (ring && (atoi(ring) == 4 || atoi(ring) == 8)) p->ring = atoi(ring);
+  // Pixel ranges, each at least four stages long: with the 8-stage ring
+  // (one workgroup per CU) at most one workgroup per CU; otherwise about
+  // two per CU.
+  int64_t splits = (p->dma && p->ring == 8) ? kWgTargetBlocks / 2 / tiles
+                                            : (kWgTargetBlocks + tiles - 1) / tiles;
   const int64_t max_splits = (p->M + 4 * bm - 1) / (4 * bm);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -931,11 +965,7 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->ws_bytes = splits > 1 ? static_cast<size_t>(splits * p->lp * 4) : 0;
   p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
-  // FCONV_WGRAD_KERNEL=staged (environment) pins the register-staged
-  // kernel on shapes the direct-to-LDS kernel takes, for A/B comparisons.
-  const char* force = getenv("FCONV_WGRAD_KERNEL");
-  p->dma = p->vec && !(force && strcmp(force, "staged") == 0);
-  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma);
+  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring);
   *out = p;
   return FCONV_OK;
 }

@@ -56,17 +56,25 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("kernel", ["default", "staged"])
+def _pin(kernel, monkeypatch):
+    if kernel == "staged":
+        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
+    elif kernel in ("ring4", "ring8"):
+        monkeypatch.setenv("FCONV_WGRAD_RING", kernel[-1])
+
+
+@pytest.mark.parametrize("kernel", ["ring4", "ring8", "staged"])
 @pytest.mark.parametrize("out_fp32", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", CASES)
 def test_wgrad_small_shapes(case, dtype, out_fp32, kernel, monkeypatch):
-    """Both kernels: the default (direct-to-LDS where C and K fill 16-byte
-    chunks) and the register-staged one (FCONV_WGRAD_KERNEL=staged)."""
+    """Every kernel: the direct-to-LDS one (where C and K fill 16-byte chunks)
+    with its 4- and 8-stage rings (FCONV_WGRAD_RING; the default is 4 for
+    bf16, 8 for fp32), and the register-staged one
+    (FCONV_WGRAD_KERNEL=staged)."""
     if dtype == "fp32" and out_fp32:
         pytest.skip("fp32 plans always write fp32")
-    if kernel == "staged":
-        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
+    _pin(kernel, monkeypatch)
     N, H, W, C, K, R, S, stride, padding = case
     dev = device()
     plan = fc.WgradPlan(N, H, W, C, K, R, S, stride, padding, dtype, out_fp32=out_fp32)
@@ -112,12 +120,11 @@ def test_wgrad_is_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("kernel", ["default", "staged"])
+@pytest.mark.parametrize("kernel", ["ring4", "ring8", "staged"])
 @pytest.mark.parametrize("name", list(wl.WGRAD_LAYERS))
 def test_wgrad_full_workload(name, kernel, monkeypatch):
     """The full benchmark workloads, every element against the oracle."""
-    if kernel == "staged":
-        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
+    _pin(kernel, monkeypatch)
     dev = device()
     L = wl.WGRAD_LAYERS[name]
     inp = wl.make_wgrad_inputs(L)
@@ -130,3 +137,38 @@ def test_wgrad_full_workload(name, kernel, monkeypatch):
     e = float_error(got, ref)
     say("  normwise error", e)
     assert e <= TOL["fp32"], (name, e)
+
+
+@pytest.mark.parametrize("name", ["wgrad_3x3_bf16", "wgrad_3x3_64_bf16"])
+def test_wgrad_graph_replay_matches_eager(name):
+    """A captured HIP graph of gradient runs (main kernel and the sum of the
+    pixel ranges), replayed several times with eager work and
+    synchronisation in between, reproduces the eager dw bit for bit."""
+    dev = device()
+    L = wl.WGRAD_LAYERS[name]
+    inp = wl.make_wgrad_inputs(L, N=4)
+    plan = fc.WgradPlan(4, L.H, L.W, L.C, L.K, L.R, L.S, L.stride, L.padding, L.dtype,
+                        out_fp32=True)
+    say("wgrad graph replay", name, plan.kernel_name, "ws", plan.workspace_bytes)
+    x, dy = to_dev(inp.x, dev), to_dev(inp.dy, dev)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    dw_eager = torch.empty(plan.dw_shape, dtype=torch.float32, device=dev)
+    plan.run(x, dy, dw_eager, ws)
+    torch.cuda.synchronize()
+    ref = dw_eager.cpu()
+    dw = torch.zeros(plan.dw_shape, dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(3):
+                assert plan.run_raw(x, dy, dw, ws, stream=s) == 0
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dw.fill_(float(rep + 1))  # eager work between replays
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.cpu(), ref), "replay %d differs" % rep

@@ -80,7 +80,7 @@ def test_workloads_and_workspace():
         kg_k = L.R * L.S * L.C * L.K
         # partial sums: a whole number of fp32 dW copies (or none)
         assert g.workspace_bytes % (4 * ((kg_k + 3) // 4)) == 0
-        assert g.kernel_name.startswith("wgrad_dma_" + ("bf16" if L.dtype == "bf16" else "f32"))
+        assert g.kernel_name.startswith("wgrad_dma_bf16" if L.dtype == "bf16" else "wgrad_dma8_f32")
 
 
 def test_run_checks_arguments():
@@ -114,3 +114,33 @@ def test_binding_refuses_host_tensors():
     g = fc.WgradPlan(1, 4, 4, 8, 8, 3, 3, 1, "SAME", "fp32")
     with pytest.raises(ValueError):
         g(torch.zeros(1, 4, 4, 8), torch.zeros(1, 4, 4, 8))
+
+
+def test_create_rejects_tensors_of_2gib_or_more():
+    # x of 2^31 bytes or more (bf16): buffer offsets are 32-bit.
+    assert _create(_desc(N=1024, H=256, W=256, C=32)) == _abi.FCONV_ERR_UNSUPPORTED
+    # dy likewise, through K.
+    assert _create(_desc(N=1024, H=64, W=64, C=16, K=256)) == _abi.FCONV_ERR_UNSUPPORTED
+    assert _create(_desc(N=64, H=64, W=64, C=16, K=256)) == _abi.FCONV_OK
+
+
+def test_staged_kernel_can_be_pinned(monkeypatch):
+    monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
+    g = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
+    assert g.kernel_name == "wgrad_bf16_128"
+    monkeypatch.delenv("FCONV_WGRAD_KERNEL")
+    g4 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
+    assert g4.kernel_name == "wgrad_dma_bf16_128"
+    assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "fp32").kernel_name == \
+        "wgrad_dma8_f32_128"
+    monkeypatch.setenv("FCONV_WGRAD_RING", "8")
+    g = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
+    assert g.kernel_name == "wgrad_dma8_bf16_128"
+    # the 8-stage ring runs one workgroup per CU: half the pixel ranges
+    assert g4.workspace_bytes > g.workspace_bytes
+    monkeypatch.setenv("FCONV_WGRAD_RING", "4")
+    assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "fp32").kernel_name == \
+        "wgrad_dma_f32_128"
+    monkeypatch.delenv("FCONV_WGRAD_RING")
+    g = fc.WgradPlan(2, 7, 6, 3, 5, 3, 3, 1, "SAME", "bf16")
+    assert g.kernel_name == "wgrad_bf16_64_elem"
