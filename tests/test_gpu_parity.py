@@ -341,3 +341,17 @@ def test_graph_replay_matches_eager(name):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.cpu(), ref), "replay %d differs" % rep
+
+
+@pytest.mark.parametrize("C,K,R", [(128, 64, 3), (64, 128, 7), (24, 40, 4), (256, 256, 1)])
+@pytest.mark.parametrize("variant", [None, "general", "tile", "rf"])
+@pytest.mark.parametrize("dtype", ["int8", "bf16", "fp32"])
+def test_full_size_valid(C, K, R, variant, dtype, monkeypatch):
+    """Filter as large as the image, VALID: every output is one dot product
+    over the whole image, the second GEMM special case of the fused op
+    (x viewed as [N, H*W*C] times w viewed as [R*S*C, K]).  Each kernel
+    family where the shape allows it."""
+    if variant is not None:
+        monkeypatch.setenv("FCONV_FORCE_VARIANT", variant)
+    test_tile_shapes(C, K, R, R, R, 1, "VALID", dtype)
+
