@@ -172,3 +172,25 @@ def test_wgrad_graph_replay_matches_eager(name):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(dw.cpu(), ref), "replay %d differs" % rep
+
+
+@pytest.mark.parametrize("shape", [
+    (8, 56, 56, 128, 128, 3, 3, 2, "SAME"),   # the strided layer's geometry (pads 0/1)
+    (4, 28, 28, 256, 64, 1, 1, 1, "VALID"),   # 1x1: a plain GEMM over the pixels
+    (2, 30, 30, 64, 96, 5, 5, 1, "SAME"),     # 5x5, K neither 64 nor a multiple of 128
+])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_wgrad_layer_shapes(shape, dtype):
+    """Larger layers of other geometries, every element against the oracle."""
+    N, H, W, C, K, R, S, stride, padding = shape
+    dev = device()
+    plan = fc.WgradPlan(N, H, W, C, K, R, S, stride, padding, dtype, out_fp32=True)
+    say("wgrad layer", shape, dtype, plan.kernel_name, "ws", plan.workspace_bytes)
+    rng = np.random.default_rng(sum(shape[:7]) * 7 + (dtype == "bf16"))
+    x = draw(rng, (N, H, W, C), dtype)
+    dy = draw(rng, plan.dy_shape, dtype)
+    got = run_wgrad(plan, x, dy, dev)
+    ref = oracle.wgrad(x, dy, R, S, stride, padding)
+    e = float_error(got, ref)
+    say("  normwise error", e)
+    assert e <= TOL["fp32"], (shape, dtype, e)
