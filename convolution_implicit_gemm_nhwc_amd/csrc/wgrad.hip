@@ -16,13 +16,19 @@
 //
 // Matrix-core mapping.  The 16x16 MFMA wants, per lane, a 16-byte run of the
 // reduction index for one row (A) and one column (B).  Both operands arrive
-// pixel-major (NHWC: the channels of one pixel are contiguous), so the
-// loader transposes in registers: a lane fetches the same 16-byte channel
-// chunk of E consecutive pixels (E = 8 bf16 / 4 fp32), transposes the E x E
-// block, and writes E pixel runs, one per channel, to LDS rows of 128 bytes
-// (one row per channel, one 16-byte slot per E pixels).  Fragment reads are
-// then single ds_read_b128s.  A = dy (rows k), B = patch (cols kk), so a lane
-// ends with 4 consecutive output channels of one (r, s, c): one 16-byte store.
+// pixel-major (NHWC: the channels of one pixel are contiguous), so every
+// fragment needs a transpose.  A = dy (rows k), B = patch (cols kk), so a
+// lane ends with 4 consecutive output channels of one (r, s, c): one
+// 16-byte store.  Two kernels:
+//  - wgrad_dma_kernel (C and K multiples of the 16-byte chunk): both
+//    operands are copied buffer->LDS in their natural layout, and bf16
+//    fragments come from gfx950's transposed LDS read; fp32 fragments hold
+//    one element per lane and need no transpose.
+//  - wgrad_kernel (any shape; also under FCONV_WGRAD_KERNEL=staged): a lane
+//    fetches the same 16-byte channel chunk of E consecutive pixels (E = 8
+//    bf16 / 4 fp32) into registers, transposes the E x E block and writes E
+//    pixel runs, one per channel, to LDS rows of 128 bytes; fragment reads
+//    are then single ds_read_b128s.
 //
 // Work split.  A workgroup owns a TK x 128 tile of dw over one range of
 // pixels.  When tiles alone do not fill the chip, the pixels are split into
@@ -135,28 +141,6 @@ __device__ inline f32x4 wg_mma(i32x4 a, i32x4 b, f32x4 c) {
 // rows one transposed write touches (E apart).
 __device__ inline int wg_slot(int row, int chunk) {
   return chunk ^ ((row ^ (row >> 3)) & 7);
-}
-
-// Transpose an E x E block held as E chunks (chunk e = pixel e's E channels)
-// into E chunks (chunk j = channel j's E pixels).
-template <int DT, int E>
-__device__ inline void wg_transpose(const i32x4 (&v)[E], i32x4 (&o)[E]) {
-  if constexpr (DT == FCONV_BF16) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        o[j][d] = static_cast<int32_t>(__builtin_amdgcn_perm(
-            static_cast<uint32_t>(v[2 * d + 1][j >> 1]), static_cast<uint32_t>(v[2 * d][j >> 1]),
-            sel));
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[j][e] = v[e][j];
-  }
 }
 
 // Store a wave's accumulators: lane holds D[k][kk] for k = k0 + 64 wk +
