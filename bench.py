@@ -40,9 +40,11 @@ KERNEL_SOURCES = [os.path.join(ROOT, "convolution_implicit_gemm_nhwc_amd", "csrc
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources the counters were taken on (the forward
+    kernels' by default; an entry may name its own files)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if sources is None else [os.path.join(ROOT, x) for x in sources]):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -68,7 +70,8 @@ def measured_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("kernel") != kernel or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("kernel") != kernel or \
+            e.get("source_hash") != kernel_source_hash(e.get("sources")):
         return None
     return e.get("bytes_per_launch")
 
@@ -235,10 +238,12 @@ def bench_wgrad(args):
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
                   "event_us_per_step": round(eager_ms * 1e3, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(L.name, kernels),
                      "kernel": kernels, "kernel_avg_us": round(step_ms * 1e3, 3),
                      "note": "one step = the main kernel and the fixed-order sum of its "
-                             "pixel ranges, timed together",
+                             "pixel ranges, timed together; traffic is the step's (both "
+                             "kernels, the partial sums' round trip included)",
                      "algorithmic_bytes_per_launch": alg_bytes},
     }
     if not args.no_cpu_baseline:
