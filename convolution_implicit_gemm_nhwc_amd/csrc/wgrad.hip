@@ -527,9 +527,10 @@ struct DmaCfg {
   static constexpr int RB_P = kWgTKK * ES;               // bytes per patch row
   static constexpr int DY_BYTES = BM * RB_DY;
   static constexpr int SB = DY_BYTES + BM * RB_P;        // stage bytes
+  static constexpr int NW = TK == 256 ? 8 : 4;           // waves: 64x64 (or 64x32) each
   static constexpr int NC = SB / 1024;                   // 1 KiB copies per stage
-  static constexpr int NCW = NC / 4;                     // per wave
-  static_assert(SB % 4096 == 0, "stage must split into 4 waves of 1 KiB copies");
+  static constexpr int NCW = NC / NW;                    // per wave
+  static_assert(SB % (NW * 1024) == 0, "stage must split into whole 1 KiB copies per wave");
   static_assert(DY_BYTES % 1024 == 0, "dy rows must fill whole copies");
 };
 
@@ -551,14 +552,14 @@ typedef __attribute__((address_space(3))) float* lds_f32_t;
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int DT, int TK, int NBUF>
-__global__ __launch_bounds__(kWgThreads)
+__global__ __launch_bounds__(TK == 256 ? 512 : 256)  // DmaCfg::NW waves
 __attribute__((amdgpu_waves_per_eu(NBUF == 8 ? 1 : 2, 2)))  // the 8-stage ring fills a CU's LDS
 void wgrad_dma_kernel(WgArgs a) {
   using Cfg = DmaCfg<DT, TK>;
-  constexpr int ES = Cfg::ES, BM = Cfg::BM, NCW = Cfg::NCW;
+  constexpr int ES = Cfg::ES, BM = Cfg::BM, NCW = Cfg::NCW, NW = Cfg::NW;
   constexpr int E = 16 / ES;
   constexpr int WK = TK / 64;
-  constexpr int WKK = 4 / WK;
+  constexpr int WKK = NW / WK;
   constexpr int NI = 4;
   constexpr int NJ = kWgTKK / WKK / 16;
   static_assert(NBUF == 4 || NBUF == 8, "ring of 4 or 8 stages");
@@ -594,14 +595,14 @@ void wgrad_dma_kernel(WgArgs a) {
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
 
-  // This wave's copies: q = wave + 4 i.  Lane l of copy q fills stage bytes
+  // This wave's copies: q = wave + NW i.  Lane l of copy q fills stage bytes
   // q * 1024 + 16 l: pixel row p and stored slot s' there, i.e. the chunk
   // s = s' ^ swz(p) of that row.
   int c_p[NCW], c_col[NCW], c_dr[NCW], c_ds[NCW], c_c[NCW];
   bool c_ok[NCW];
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
-    const int q = wave + 4 * i;
+    const int q = wave + NW * i;
     const int byte = q * 1024 + lane * 16;
     const bool isdy = q * 1024 < Cfg::DY_BYTES;  // wave-uniform
     const int rb = isdy ? Cfg::RB_DY : Cfg::RB_P;
@@ -629,7 +630,7 @@ void wgrad_dma_kernel(WgArgs a) {
     const int mb = m_begin + st * BM;
 #pragma unroll
     for (int i = 0; i < NCW; ++i) {
-      const int q = wave + 4 * i;
+      const int q = wave + NW * i;
       const int m = mb + c_p[i];
       const bool live = c_ok[i] && st < nst && m < m_end;
       uint32_t off = kOutOfRange;
@@ -828,12 +829,14 @@ hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
 template <int DT, int TK, int NBUF>
 hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
   const int grid = (a.blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF>), dim3(grid), dim3(kWgThreads), 0, s, a);
+  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF>), dim3(grid), dim3(DmaCfg<DT, TK>::NW * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
+  if (p->dma && p->tk == 256) return launch_wgrad_dma<DT, 256, 4>(a, s);
   if (p->dma)
     return p->ring == 8
                ? (p->tk == 128 ? launch_wgrad_dma<DT, 128, 8>(a, s) : launch_wgrad_dma<DT, 64, 8>(a, s))
@@ -852,6 +855,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
 const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring) {
+  if (dma && tk == 256) return "wgrad_dma_bf16_256";
   if (dma && ring == 8) {
     if (dtype == FCONV_BF16) return tk == 128 ? "wgrad_dma8_bf16_128" : "wgrad_dma8_bf16_64";
     return tk == 128 ? "wgrad_dma8_f32_128" : "wgrad_dma8_f32_64";
@@ -908,14 +912,11 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   }
   p->Kg = static_cast<int32_t>(kg);
   p->vec = d.C % p->E == 0 && d.K % p->E == 0;
-  p->tk = d.K > 64 ? 128 : 64;
-  p->tiles_k = (d.K + p->tk - 1) / p->tk;
-  p->tiles_kk = (p->Kg + kWgTKK - 1) / kWgTKK;
-  const int64_t tiles = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
   const int64_t bm = 8 * p->E;
   // FCONV_WGRAD_KERNEL=staged (environment) pins the register-staged
   // kernel on shapes the direct-to-LDS kernel takes; FCONV_WGRAD_RING=4|8
-  // its LDS ring depth (both for A/B comparisons).
+  // its LDS ring depth; FCONV_WGRAD_TK=128 the 128-channel tile where the
+  // 256-channel one would be chosen (all for A/B comparisons).
   const char* force = getenv("FCONV_WGRAD_KERNEL");
   p->dma = p->vec && !(force && strcmp(force, "staged") == 0);
   // Ring depth: bf16 runs two workgroups per CU with 4-stage rings (the
@@ -926,11 +927,21 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   const char* ring = getenv("FCONV_WGRAD_RING");
   p->ring = d.dtype == FCONV_FP32 ? 8 : 4;
   if (ring && (atoi(ring) == 4 || atoi(ring) == 8)) p->ring = atoi(ring);
-  // Pixel ranges, each at least four stages long: with the 8-stage ring
-  // (one workgroup per CU) at most one workgroup per CU; otherwise about
-  // two per CU.
-  int64_t splits = (p->dma && p->ring == 8) ? kWgTargetBlocks / 2 / tiles
-                                            : (kWgTargetBlocks + tiles - 1) / tiles;
+  // Tile width: 256 output channels (eight waves, one workgroup per CU,
+  // a quarter fewer operand bytes per flop) for bf16 with K > 128 on the
+  // 4-stage ring; else 128, or 64 for K <= 64.
+  const char* tk_env = getenv("FCONV_WGRAD_TK");
+  const bool wide = p->dma && d.dtype == FCONV_BF16 && p->ring == 4 && d.K > 128 &&
+                    !(tk_env && atoi(tk_env) == 128);
+  p->tk = wide ? 256 : d.K > 64 ? 128 : 64;
+  p->tiles_k = (d.K + p->tk - 1) / p->tk;
+  p->tiles_kk = (p->Kg + kWgTKK - 1) / kWgTKK;
+  const int64_t tiles = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
+  // Pixel ranges, each at least four stages long: one workgroup per CU with
+  // the 8-stage ring or the 256-channel tile, else about two per CU.
+  const bool one_per_cu = p->dma && (p->ring == 8 || p->tk == 256);
+  int64_t splits = one_per_cu ? kWgTargetBlocks / 2 / tiles
+                              : (kWgTargetBlocks + tiles - 1) / tiles;
   const int64_t max_splits = (p->M + 4 * bm - 1) / (4 * bm);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;

@@ -129,8 +129,12 @@ def test_staged_kernel_can_be_pinned(monkeypatch):
     g = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g.kernel_name == "wgrad_bf16_128"
     monkeypatch.delenv("FCONV_WGRAD_KERNEL")
+    assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16").kernel_name == \
+        "wgrad_dma_bf16_256"
+    monkeypatch.setenv("FCONV_WGRAD_TK", "128")
     g4 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g4.kernel_name == "wgrad_dma_bf16_128"
+    monkeypatch.delenv("FCONV_WGRAD_TK")
     assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "fp32").kernel_name == \
         "wgrad_dma8_f32_128"
     monkeypatch.setenv("FCONV_WGRAD_RING", "8")
