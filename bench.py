@@ -25,6 +25,7 @@ cores on the same workload.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -40,13 +41,21 @@ KERNEL_SOURCES = [os.path.join(ROOT, "convolution_implicit_gemm_nhwc_amd", "csrc
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and blank lines: what the compiler
+    turns into kernels (a comment edit leaves the counters valid)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(sources=None) -> str:
-    """Hash of the kernel sources the counters were taken on (the forward
-    kernels' by default; an entry may name its own files)."""
+    """Hash of the code of the kernel sources the counters were taken on (the
+    forward kernels' by default; an entry may name its own files)."""
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES if sources is None else [os.path.join(ROOT, x) for x in sources]):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -59,7 +59,7 @@ struct fconv_wgrad_plan_s {
   bool vec;          // C % E == 0 and K % E == 0: 16-byte gathers
   bool dma;          // vec shapes: the direct-to-LDS kernel (else register-staged)
   int32_t ring;      // direct-to-LDS kernel: stages in its LDS ring (4 or 8)
-  int32_t tk;        // output channels per tile (64 or 128)
+  int32_t tk;        // output channels per tile (64, 128, or 256 with 8 waves)
   int32_t tiles_k, tiles_kk;
   int32_t splits;    // pixel ranges
   int32_t m_per_split;
@@ -77,7 +77,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWgThreads = 256;   // 4 waves
+constexpr int kWgThreads = 256;   // register-staged kernel: 4 waves
 constexpr int kWgTKK = 128;       // (r,s,c) columns per tile
 constexpr int kWgRowBytes = 128;  // one LDS row: 8 slots of 16 bytes
 constexpr int kWgTargetBlocks = 512;  // two workgroups per CU (256 CUs)
@@ -514,11 +514,12 @@ void wgrad_kernel(WgArgs a) {
 // bytes.  fp32: a read touches 4 rows, 64 bytes each; swz(p) = 4 (p & 3)
 // separates them.
 //
-// Pipeline (as the forward tiled kernel): four LDS stage buffers, each its
-// own __shared__ array; copies run three stages ahead; a step waits for its
-// own copies of the stage, meets the other waves at a plain barrier, issues
-// the copies three stages ahead into the buffer of the stage before, reads
-// the stage's fragments and runs its MFMAs.
+// Pipeline (as the forward tiled kernel): NBUF LDS stage buffers (4, or 8
+// for fp32 at one workgroup per CU), each its own __shared__ array; copies
+// run NBUF - 1 stages ahead; a step waits for its own copies of the stage,
+// meets the other waves at a plain barrier, issues the copies NBUF - 1
+// stages ahead into the buffer of the stage before, reads the stage's
+// fragments and runs its MFMAs.
 template <int DT, int TK>
 struct DmaCfg {
   static constexpr int ES = DT == FCONV_BF16 ? 2 : 4;
