@@ -214,7 +214,6 @@ def bench_wgrad(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = g0.elapsed_time(g1) / args.steps
-    dw_gpu = dw.cpu().numpy()
 
     ops = L.ops_count()
     esize = 2 if L.dtype == "bf16" else 4
@@ -268,7 +267,6 @@ def bench_wgrad(args):
         out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
-    del dw_gpu
     print(json.dumps(out), flush=True)
 
 

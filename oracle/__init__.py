@@ -45,37 +45,41 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def _bind(lib):
+    """Declare the C signatures on a loaded oracle library; returns it."""
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.oracle_geometry.argtypes = [i, i, i, i, i, i, i, p]
+    lib.oracle_output_hw.argtypes = [p, p]
+    for name in ("oracle_conv_i8_direct", "oracle_conv_i8_im2col",
+                 "oracle_conv_f32_direct", "oracle_conv_bf16_direct"):
+        getattr(lib, name).argtypes = [p, p, p, p]
+        getattr(lib, name).restype = i
+    lib.oracle_epilogue_i8.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p,
+                                       ctypes.c_float, p, i, p]
+    lib.oracle_epilogue_i8.restype = None
+    lib.oracle_epilogue_i8_ex.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p, p,
+                                          ctypes.c_float, p, i, i, p]
+    lib.oracle_epilogue_i8_ex.restype = None
+    lib.oracle_epilogue_float.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
+                                          ctypes.c_float, i, p]
+    lib.oracle_epilogue_float.restype = None
+    lib.oracle_epilogue_float_ex.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
+                                             ctypes.c_float, i, ctypes.c_float,
+                                             ctypes.c_float, p]
+    lib.oracle_epilogue_float_ex.restype = None
+    lib.oracle_wgrad_direct.argtypes = [p, p, p, p]
+    lib.oracle_wgrad_direct.restype = i
+    lib.oracle_num_threads.restype = i
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
-        p = ctypes.c_void_p
-        i = ctypes.c_int
-        lib.oracle_geometry.argtypes = [i, i, i, i, i, i, i, p]
-        lib.oracle_output_hw.argtypes = [p, p]
-        for name in ("oracle_conv_i8_direct", "oracle_conv_i8_im2col",
-                     "oracle_conv_f32_direct", "oracle_conv_bf16_direct"):
-            getattr(lib, name).argtypes = [p, p, p, p]
-            getattr(lib, name).restype = i
-        lib.oracle_epilogue_i8.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p,
-                                           ctypes.c_float, p, i, p]
-        lib.oracle_epilogue_i8.restype = None
-        lib.oracle_epilogue_i8_ex.argtypes = [p, ctypes.c_long, i, ctypes.c_float, p, p,
-                                              ctypes.c_float, p, i, i, p]
-        lib.oracle_epilogue_i8_ex.restype = None
-        lib.oracle_epilogue_float.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
-                                              ctypes.c_float, i, p]
-        lib.oracle_epilogue_float.restype = None
-        lib.oracle_epilogue_float_ex.argtypes = [p, ctypes.c_long, i, p, p, p, p, p,
-                                                 ctypes.c_float, i, ctypes.c_float,
-                                                 ctypes.c_float, p]
-        lib.oracle_epilogue_float_ex.restype = None
-        lib.oracle_wgrad_direct.argtypes = [p, p, p, p]
-        lib.oracle_wgrad_direct.restype = i
-        lib.oracle_num_threads.restype = i
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
     return _lib
 
 
