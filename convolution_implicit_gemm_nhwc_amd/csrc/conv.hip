@@ -683,7 +683,7 @@ constexpr int kTileBuf = (kTileBM + kTileBN) * kTileStage;  // 32 KiB
 
 constexpr int kTileThreads = 512;
 
-template <int DT, bool KVEC>
+template <int DT, bool KVEC, bool DS>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_tile_kernel(ConvArgs a) {
   using Acc = typename Dt<DT>::Acc;
@@ -871,6 +871,44 @@ void conv_tile_kernel(ConvArgs a) {
   barrier();
   read_frags(buf0, fa);
   int st = 0;
+  if constexpr (DS) {
+    // DS: two stages per barrier.  Every copy (stages st + 1 and st + 2) and
+    // every LDS read has completed before it, then stages st + 3 and st + 4
+    // are copied into the buffers of st - 1 and st (both read during the
+    // previous double step), stage st is computed from cur while st + 1's
+    // fragments are read, then st + 1 from them while st + 2's are read
+    // into cur.
+    auto dstep = [&](const char* b1, const char* b2, char* c3, char* c4)
+        __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      barrier();
+      issue(c3);
+      issue(c4);
+      read_frags(b1, fb);
+      mma(fa);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(b2, fa);
+      mma(fb);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; st + 4 <= nst; st += 4) {
+      dstep(buf1, buf2, buf3, buf0);
+      dstep(buf3, buf0, buf1, buf2);
+    }
+    if (st + 2 <= nst) {
+      dstep(buf1, buf2, buf3, buf0);
+      st += 2;
+    }
+    if (st < nst) mma(fa);  // the last stage, read by the double step before
+  } else {
   for (; st + 4 <= nst; st += 4) {
     step(buf1, buf3, fa, fb);
     step(buf2, buf0, fb, fa);
@@ -880,6 +918,7 @@ void conv_tile_kernel(ConvArgs a) {
   if (st < nst) step(buf1, buf3, fa, fb);
   if (st + 1 < nst) step(buf2, buf0, fb, fa);
   if (st + 2 < nst) step(buf3, buf1, fa, fb);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
   if (ch0 >= a.K) return;
@@ -1813,7 +1852,14 @@ template <int DT>
 hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((p->M + kTileBM - 1) / kTileBM),
                   static_cast<unsigned>((p->Kp + kTileBN - 1) / kTileBN));
-  hipLaunchKernelGGL((conv_tile_kernel<DT, true>), grid, dim3(kTileThreads), 0, s, a);
+  // Two stages per barrier where measured faster or equal: the layers with
+  // one 128-channel tile (K <= 128: 4% on the CBNA 5x5 and 7x7 layers, equal
+  // on the strided int8 layer); one per stage otherwise (3% slower with two
+  // on the 256-channel bf16 layer).
+  if (p->d.K <= kTileBN)
+    hipLaunchKernelGGL((conv_tile_kernel<DT, true, true>), grid, dim3(kTileThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_tile_kernel<DT, true, false>), grid, dim3(kTileThreads), 0, s, a);
   return hipGetLastError();
 }
 
