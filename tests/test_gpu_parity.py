@@ -133,6 +133,12 @@ def test_fuzz_small_shapes(dtype, count, seed):
 def test_tile_shapes(C, K, H, W, R, stride, pad, dtype):
     """Channel counts on and off the vector widths, several 64-channel blocks,
     ragged pixel tails."""
+    check_case(tile_case(C, K, H, W, R, stride, pad, dtype), dtype)
+
+
+def tile_case(C, K, H, W, R, stride, pad, dtype):
+    """Seeded inputs of one layer: int8 with side input and bias, or bf16 /
+    fp32 with bias, batch norm and ReLU."""
     rng = np.random.default_rng(C * 1000 + K)
     Ho, Wo = oracle.geometry(H, W, R, R, stride, stride, pad == "SAME")[:2]
     N = 3
@@ -156,6 +162,12 @@ def test_tile_shapes(C, K, H, W, R, stride, pad, dtype):
         c = dict(shape=(N, H, W, C, K, R, R, stride, pad), x=x, w=w,
                  bias=rng.normal(0, .1, K).astype(np.float32), side=None, cis=1.0, sis=0.0,
                  relu=True, ops=[wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], bn=bn, use_bias=True)
+    return c
+
+
+def check_case(c, dtype):
+    """Run one case on the GPU against the oracle (int8 bit-exact, bf16 2e-2,
+    fp32 2e-6 normwise); returns the plan's kernel."""
     say("tile shape %s %s" % (dtype, c["shape"]))
     y, r, guards, plan = _run_case(c, dtype)
     assert guards
@@ -163,6 +175,7 @@ def test_tile_shapes(C, K, H, W, R, stride, pad, dtype):
         assert np.array_equal(y, r), "%d differ" % np.count_nonzero(y != r)
     else:
         assert float_error(y, r) <= (TOL["bf16"] if dtype == "bf16" else 2e-6)
+    return plan.kernel_name
 
 
 def test_crafted_fma_and_contraction_cases():
@@ -355,3 +368,18 @@ def test_full_size_valid(C, K, R, variant, dtype, monkeypatch):
         monkeypatch.setenv("FCONV_FORCE_VARIANT", variant)
     test_tile_shapes(C, K, R, R, R, 1, "VALID", dtype)
 
+
+
+@pytest.mark.parametrize("K", [64, 256])
+@pytest.mark.parametrize("dtype,C,R,stages", [
+    ("int8", 128, 1, 1), ("int8", 256, 1, 2), ("fp32", 96, 1, 3), ("int8", 128, 2, 4),
+    ("fp32", 160, 1, 5), ("fp32", 224, 1, 7), ("bf16", 64, 3, 9)])
+def test_tile_stage_counts(dtype, C, R, stages, K, monkeypatch):
+    """The tiled kernel's loop tails: every stage count from 1 to 9 modulo
+    the 4-buffer ring, with one 128-channel tile (K = 64: two stages per
+    barrier) and with two (K = 256: one stage per barrier)."""
+    esize = {"int8": 1, "bf16": 2, "fp32": 4}[dtype]
+    assert R * R * C * esize // 128 == stages
+    monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
+    name = check_case(tile_case(C, K, 7, 9, R, 1, "SAME", dtype), dtype)
+    assert name.startswith("conv_tile_"), name
