@@ -696,6 +696,9 @@ void conv_tile_kernel(ConvArgs a) {
   __shared__ __attribute__((aligned(1024))) char buf1[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf2[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf3[kTileBuf];
+  // Float epilogue: the tile's 128 channels of bias, gamma, var, mean and
+  // beta, one 1 KiB slot each (512 bytes used), copied before stage 0.
+  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 16 : 5 * 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -754,7 +757,18 @@ void conv_tile_kernel(ConvArgs a) {
                                                      : i32x4{0, 0, 0, 0};
     }
   } else {
-    fpar.load(a, ch_live ? ch0 : a.K, KVEC && ch_live);  // nothing loaded past K
+    // Waves 0-4 copy one vector each, before their stage copies, so the
+    // waits for stage 0 cover them (zeros past K and for an absent op).
+    if (wave < 5) {
+      const float* src = wave == 0 ? a.bias : wave == 1 ? a.bn_gamma : wave == 2 ? a.bn_var
+                       : wave == 3 ? a.bn_mean : a.bn_beta;
+      const bool use = wave == 0 ? a.use_bias != 0 : a.use_bn != 0;
+      const __amdgpu_buffer_rsrc_t pr =
+          make_rsrc(use ? src : nullptr, use ? static_cast<uint32_t>(a.K) * 4u : 0u);
+      const uint32_t off =
+          lane < 32 ? static_cast<uint32_t>((blockIdx.y * kTileBN + 4 * lane) * 4) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)(epar + wave * 1024), 16, off, 0, 0, 0);
+    }
   }
 
   const int nst = a.R * a.S * (a.C / SE);
@@ -935,6 +949,16 @@ void conv_tile_kernel(ConvArgs a) {
       epilogue_store_i8<8>(v, a, m, ch0, KVEC, side_pre[i], bias_pre, cis_pre);
     }
   } else {
+    // Per-channel values from LDS (landed before the first barrier), with
+    // the arithmetic of FloatEpiParams::load.
+    const float* ep = reinterpret_cast<const float*>(epar) + (ch0 - blockIdx.y * kTileBN);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fpar.bias[e] = a.use_bias ? ep[e] : 0.0f;
+      fpar.sc[e] = a.use_bn ? ep[256 + e] / __builtin_sqrtf(ep[512 + e] + a.bn_eps) : 0.0f;
+      fpar.mean[e] = a.use_bn ? ep[768 + e] : 0.0f;
+      fpar.beta[e] = a.use_bn ? ep[1024 + e] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
