@@ -552,7 +552,7 @@ typedef __attribute__((address_space(3))) float* lds_f32_t;
 // [15:14]; expcnt and lgkmcnt at their maximum, i.e. not waited on).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int DT, int TK, int NBUF, bool PAIRS>
+template <int DT, int TK, int NBUF>
 __global__ __launch_bounds__(TK == 256 ? 512 : 256)  // DmaCfg::NW waves
 __attribute__((amdgpu_waves_per_eu(NBUF == 8 ? 1 : 2, 2)))  // the 8-stage ring fills a CU's LDS
 void wgrad_dma_kernel(WgArgs a) {
@@ -739,70 +739,46 @@ void wgrad_dma_kernel(WgArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // Own copies of the stage landed: the NBUF - 2 later stages' may still be
-  // in flight.
-  auto wait_stage = [&]() {
-    constexpr int imm = vmcnt_imm((NBUF - 2) * NCW);
+  int st = 0;
+  // Stage st lives in buffer st % NBUF.  Two stages per barrier (3-6%
+  // faster than one on the bf16 layers, 1% on fp32): this wave's copies of
+  // stages st and st + 1 have landed before it (those of the NBUF - 4 later
+  // stages may still be in flight), then stages st + NBUF - 2 and
+  // st + NBUF - 1 are copied into the buffers of st - 2 and st - 1
+  // (consumed by the previous double step's MFMAs).
+  auto dwait = [&]() __attribute__((always_inline)) {
+    constexpr int imm = vmcnt_imm((NBUF - 4) * NCW);
     __builtin_amdgcn_s_waitcnt(imm);
   };
-  auto step = [&](const char* cur, char* ahead) __attribute__((always_inline)) {
-    wait_stage();
+  auto dstep = [&](const char* c0, const char* c1, char* f0, char* f1)
+      __attribute__((always_inline)) {
+    dwait();
     barrier();
-    issue(ahead);
-    mma_stage(cur);
-    // The MFMAs (and so the LDS reads they consume) stay ahead of the next
-    // step's barrier, after which another wave's copies reuse this buffer.
+    issue(f0);
+    issue(f1);
+    mma_stage(c0);
+    mma_stage(c1);
     __builtin_amdgcn_sched_barrier(0);
   };
-
-  int st = 0;
-  if constexpr (PAIRS) {
-    static_assert(NBUF == 4, "two stages per barrier on the 4-stage ring");
-    // Two stages per barrier: every copy (stages st and st + 1) has landed
-    // before it, then stages st + 2 and st + 3 are copied into the buffers of
-    // st - 2 and st - 1 (consumed by the previous double step's MFMAs).
-    auto dstep = [&](const char* c0, const char* c1, char* f0, char* f1)
-        __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(0);
-      barrier();
-      issue(f0);
-      issue(f1);
-      mma_stage(c0);
-      mma_stage(c1);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    issue(bufs[0]);
-    issue(bufs[1]);
-    for (; st + 4 <= nst; st += 4) {
-      dstep(bufs[0], bufs[1], bufs[2], bufs[3]);
-      dstep(bufs[2], bufs[3], bufs[0], bufs[1]);
-    }
-    if (st + 2 <= nst) {
-      dstep(bufs[0], bufs[1], bufs[2], bufs[3]);
-      st += 2;
-      if (st < nst) {
-        __builtin_amdgcn_s_waitcnt(0);
-        barrier();
-        mma_stage(bufs[2]);
-      }
-    } else if (st < nst) {
-      __builtin_amdgcn_s_waitcnt(0);
-      barrier();
-      mma_stage(bufs[0]);
-    }
-  } else {
-  // Stage st lives in buffer st % NBUF; step st copies stage st + NBUF - 1
-  // into the buffer of stage st - 1.  Whole trips of NBUF steps in the loop,
-  // the rest after it; past the last stage the copies are zeros.
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) issue(bufs[i]);
+  for (int i = 0; i < NBUF - 2; ++i) issue(bufs[i]);
   for (; st + NBUF <= nst; st += NBUF) {
 #pragma unroll
-    for (int i = 0; i < NBUF; ++i) step(bufs[i], bufs[(i + NBUF - 1) % NBUF]);
+    for (int i = 0; i < NBUF; i += 2)
+      dstep(bufs[i], bufs[i + 1], bufs[(i + NBUF - 2) % NBUF], bufs[(i + NBUF - 1) % NBUF]);
   }
+  // The rest: whole double steps, then a last single stage.
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (st + i < nst) step(bufs[i], bufs[(i + NBUF - 1) % NBUF]);
+  for (int i = 0; i < NBUF - 2; i += 2)
+    if (st + i + 2 <= nst)
+      dstep(bufs[i], bufs[i + 1], bufs[(i + NBUF - 2) % NBUF], bufs[(i + NBUF - 1) % NBUF]);
+  const int rest = (nst - st) & ~1;  // stages done by the double steps above
+  if (st + rest < nst) {
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier();
+#pragma unroll
+    for (int i = 0; i < NBUF; i += 2)
+      if (i == rest) mma_stage(bufs[i]);
   }
   __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
@@ -866,10 +842,8 @@ hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
 template <int DT, int TK, int NBUF>
 hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
   const int grid = (a.blocks + 7) / 8 * 8;
-  // The 4-stage ring runs two stages per barrier (3-6% faster on the bf16
-  // layers); the 8-stage ring keeps one per stage.
-  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF, NBUF == 4>), dim3(grid),
-                     dim3(DmaCfg<DT, TK>::NW * 64), 0, s, a);
+  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF>), dim3(grid), dim3(DmaCfg<DT, TK>::NW * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
