@@ -696,9 +696,11 @@ void conv_tile_kernel(ConvArgs a) {
   __shared__ __attribute__((aligned(1024))) char buf1[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf2[kTileBuf];
   __shared__ __attribute__((aligned(1024))) char buf3[kTileBuf];
-  // Float epilogue: the tile's 128 channels of bias, gamma, var, mean and
-  // beta, one 1 KiB slot each (512 bytes used), copied before stage 0.
-  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 16 : 5 * 1024];
+  // Epilogue values, copied before stage 0: for float, the tile's 128
+  // channels of bias, gamma, var, mean and beta, one 1 KiB slot each (512
+  // bytes used); for int8, bias and the per-channel scale in the first two
+  // slots and the tile's side input (128 pixels x 128 bytes) after them.
+  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 18 * 1024 : 5 * 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -738,23 +740,31 @@ void conv_tile_kernel(ConvArgs a) {
   // side chunks) are issued here, before the first copy, so that they land
   // during the main loop (and no later than the first stage's copies).
   const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
-  const bool ch_live = ch0 < a.K;
-  float bias_pre[8], cis_pre[8];
-  i32x4 side_pre[4];
   FloatEpiParams<8> fpar;
   if constexpr (DT == FCONV_INT8) {
-    if (ch_live) {
-      load_bias<8>(a, ch0, KVEC, bias_pre);
-      load_scales<8>(a, ch0, KVEC, cis_pre);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bias_pre[e] = cis_pre[e] = 0.0f;
+    // Wave 0 copies the bias, wave 1 the per-channel scales (if any), and
+    // every wave two 1 KiB pieces of the side tile (8 pixels of 128 bytes
+    // each: lane l takes chunk l % 8 of pixel l / 8), all before their stage
+    // copies, so the waits for stage 0 cover them; zeros past K and M.
+    const int cbase = blockIdx.y * kTileBN;
+    if (wave < 2) {
+      const float* src = wave == 0 ? a.bias : a.cis_vec;
+      const __amdgpu_buffer_rsrc_t pr =
+          make_rsrc(src, src ? static_cast<uint32_t>(a.K) * 4u : 0u);
+      const uint32_t off = lane < 32 ? static_cast<uint32_t>((cbase + 4 * lane) * 4) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)(epar + wave * 1024), 16, off, 0, 0, 0);
     }
+    if (a.use_side) {
+      const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, a.side_bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
-      side_pre[i] = a.use_side && ch_live && m < a.M ? load_side_chunk<8>(a, m, ch0, KVEC)
-                                                     : i32x4{0, 0, 0, 0};
+      for (int h = 0; h < 2; ++h) {
+        const int piece = wave + 8 * h;                    // pixels 8*piece .. +7
+        const int m = blockIdx.x * kTileBM + 8 * piece + (lane >> 3);
+        const int c = cbase + 16 * (lane & 7);
+        const uint32_t off = m < a.M && c < a.K ? static_cast<uint32_t>(m * a.K + c) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(epar + 2048 + piece * 1024), 16, off,
+                                                 0, 0, 0);
+      }
     }
   } else {
     // Waves 0-4 copy one vector each, before their stage copies, so the
@@ -937,16 +947,32 @@ void conv_tile_kernel(ConvArgs a) {
 
   if (ch0 >= a.K) return;
   if constexpr (DT == FCONV_INT8) {
+    // Per-channel values and side chunks from LDS (landed before the first
+    // barrier).
+    const int cl = ch0 - blockIdx.y * kTileBN;
+    const float* eb = reinterpret_cast<const float*>(epar);
+    float bias_l[8], cis_l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bias_l[e] = eb[cl + e];
+      cis_l[e] = a.cis_vec ? eb[256 + cl + e] : a.cis;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+      const int p = wm * 64 + i * 16 + col;
+      const int m = blockIdx.x * kTileBM + p;
       if (m >= a.M) continue;
       int32_t v[8];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
-      epilogue_store_i8<8>(v, a, m, ch0, KVEC, side_pre[i], bias_pre, cis_pre);
+      i32x4 sd = i32x4{0, 0, 0, 0};
+      if (a.use_side) {
+        const i32x2 w2 = *reinterpret_cast<const i32x2*>(epar + 2048 + p * 128 + cl);
+        sd = i32x4{w2.x, w2.y, 0, 0};
+      }
+      epilogue_store_i8<8>(v, a, m, ch0, KVEC, sd, bias_l, cis_l);
     }
   } else {
     // Per-channel values from LDS (landed before the first barrier), with
