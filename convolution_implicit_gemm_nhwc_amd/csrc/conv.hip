@@ -679,41 +679,52 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint
 // wave holds two of the four 16-row MFMA tiles of a 64-row packed filter
 // block, so each lane owns 8 consecutive output channels.
 constexpr int kTileBM = 128, kTileBN = 128, kTileStage = 128;
-constexpr int kTileBuf = (kTileBM + kTileBN) * kTileStage;  // 32 KiB
 
 constexpr int kTileThreads = 512;
 
-template <int DT, bool KVEC, bool DS>
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+template <int DT, bool KVEC, bool DS, int BM>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_tile_kernel(ConvArgs a) {
+  static_assert(BM == 128 || BM == 64, "pixel rows per tile");
+  // BM = 64 (grids with at most half as many 128-pixel tiles as CUs): waves
+  // of 32 pixels x 32 channels, one pixel copy per wave per stage.
+  constexpr int PH = BM / 64;            // pixel copies per wave per stage
+  constexpr int PI = BM / 32;            // 16-pixel MFMA tiles per wave
+  constexpr int CPS = PH + 2;            // copies per wave per stage
+  constexpr int MPS = 2 * PI * 2;        // MFMAs per wave per stage
+  constexpr int TB = (BM + kTileBN) * kTileStage;  // bytes of one stage
   using Acc = typename Dt<DT>::Acc;
   constexpr int E = Dt<DT>::kChunk;
   constexpr int ES = 16 / E;
   constexpr int SE = kTileStage / ES;  // reduction elements per stage
   // Four distinct arrays, so that reading one stage never waits for the
   // copies still in flight into the others.
-  __shared__ __attribute__((aligned(1024))) char buf0[kTileBuf];
-  __shared__ __attribute__((aligned(1024))) char buf1[kTileBuf];
-  __shared__ __attribute__((aligned(1024))) char buf2[kTileBuf];
-  __shared__ __attribute__((aligned(1024))) char buf3[kTileBuf];
+  __shared__ __attribute__((aligned(1024))) char buf0[TB];
+  __shared__ __attribute__((aligned(1024))) char buf1[TB];
+  __shared__ __attribute__((aligned(1024))) char buf2[TB];
+  __shared__ __attribute__((aligned(1024))) char buf3[TB];
   // Epilogue values, copied before stage 0: for float, the tile's 128
   // channels of bias, gamma, var, mean and beta, one 1 KiB slot each (512
   // bytes used); for int8, bias and the per-channel scale in the first two
-  // slots and the tile's side input (128 pixels x 128 bytes) after them.
-  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 18 * 1024 : 5 * 1024];
+  // slots and the tile's side input (BM pixels x 128 bytes) after them.
+  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 2048 + BM * 128 : 5 * 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;  // 64-pixel half, 32-channel quarter
+  const int wm = wave & 1, wn = wave >> 1;  // pixel half, 32-channel quarter
   const int g = lane >> 4, col = lane & 15;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
 
-  // Copy role: copy h (h = 0, 1) of this wave covers pixel rows
-  // 64h + 8*wave .. +7 and copy 2+h the filter rows 128 + the same; lane l
-  // fills slot l & 7 of row 8*wave + 64h + (l >> 3), i.e. chunk
+  // Copy role: copy h (h < PH) of this wave covers pixel rows
+  // 64h + 8*wave .. +7 and filter copy h (h < 2) the filter rows BM + the
+  // same; lane l fills slot l & 7 of row 8*wave + 64h + (l >> 3), i.e. chunk
   // q = (l & 7) ^ ((l >> 3) & 7) of that row.
   const int r0 = 8 * wave + (lane >> 3);
   const int q = (lane & 7) ^ ((lane >> 3) & 7);
@@ -722,7 +733,7 @@ void conv_tile_kernel(ConvArgs a) {
   const int RS = a.wrow_bytes;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int m = blockIdx.x * kTileBM + r0 + 64 * h;
+    const int m = blockIdx.x * BM + r0 + 64 * h;
     const int mm = m < a.M ? m : 0;
     const uint32_t qq = fast_div(static_cast<uint32_t>(mm), a.wo_mul, a.wo_add, a.wo_shift);
     const int wo = mm - static_cast<int>(qq) * a.Wo;
@@ -757,9 +768,9 @@ void conv_tile_kernel(ConvArgs a) {
     if (a.use_side) {
       const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, a.side_bytes);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < PH; ++h) {
         const int piece = wave + 8 * h;                    // pixels 8*piece .. +7
-        const int m = blockIdx.x * kTileBM + 8 * piece + (lane >> 3);
+        const int m = blockIdx.x * BM + 8 * piece + (lane >> 3);
         const int c = cbase + 16 * (lane & 7);
         const uint32_t off = m < a.M && c < a.K ? static_cast<uint32_t>(m * a.K + c) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(epar + 2048 + piece * 1024), 16, off,
@@ -800,7 +811,7 @@ void conv_tile_kernel(ConvArgs a) {
     }
     const bool live = st < nst;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < PH; ++h) {
       const int hi = hb[h] + r, wi = wb[h] + s;
       const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
                       static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
@@ -812,29 +823,29 @@ void conv_tile_kernel(ConvArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (lds_ptr_t)(buf + (kTileBM + 8 * wave + 64 * h) * kTileStage), 16,
+          wr, (lds_ptr_t)(buf + (BM + 8 * wave + 64 * h) * kTileStage), 16,
           live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0, 0);
   };
 
-  Acc acc[4][2];
+  Acc acc[PI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < PI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
   // Fragment rows: pixel row wm*64 + 16i + col, filter row 128 + wn*32 +
   // 16j + col; both have (row & 7) == (col & 7).
   struct Frags {
-    i32x4 pf[2][4], ff[2][2];
+    i32x4 pf[2][PI], ff[2][2];
   };
   auto read_frags = [&](const char* buf, Frags& f) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint32_t slot = static_cast<uint32_t>(((kk * 4 + g) ^ (col & 7)) * 16);
-      const char* pl = buf + (wm * 64 + col) * kTileStage + slot;
-      const char* fb = buf + (kTileBM + wn * 32 + col) * kTileStage + slot;
+      const char* pl = buf + (wm * (BM / 2) + col) * kTileStage + slot;
+      const char* fb = buf + (BM + wn * 32 + col) * kTileStage + slot;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
+      for (int i = 0; i < PI; ++i) f.pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
 #pragma unroll
       for (int j = 0; j < 2; ++j) f.ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
     }
@@ -843,7 +854,7 @@ void conv_tile_kernel(ConvArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = mma_chunk(f.ff[kk][j], f.pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
@@ -862,7 +873,7 @@ void conv_tile_kernel(ConvArgs a) {
   // buffer the copies of stage st + 3 issued next reuse.  (__syncthreads()
   // would add a release fence that waits for all copies.)
   auto step = [&](const char* next, char* next3, const Frags& cur, Frags& nxt) {
-    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS));
     barrier();
     issue(next3);  // stage + 3, into the buffer of the stage before this one
     read_frags(next, nxt);
@@ -871,12 +882,13 @@ void conv_tile_kernel(ConvArgs a) {
     // to the end of the step, and the next step's MFMAs wait on them), then
     // the copies spread between the MFMAs, so that a copy stalled on a busy
     // memory pipe does not hold the matrix core idle.
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PI + 2), 0);  // DS read
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+    for (int q = 0; q < CPS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MPS / CPS, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
     }
+    if constexpr (MPS % CPS != 0) __builtin_amdgcn_sched_group_barrier(0x008, MPS % CPS, 0);
     // Issue every MFMA before the next step's wait and barrier (otherwise
     // the scheduler hoists the barrier above them and the MFMAs queue behind
     // the barrier wait).
@@ -891,7 +903,7 @@ void conv_tile_kernel(ConvArgs a) {
   issue(buf1);
   issue(buf2);
   Frags fa, fb;
-  __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): this wave's copies of stage 0
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPS));  // this wave's copies of stage 0
   barrier();
   read_frags(buf0, fa);
   int st = 0;
@@ -910,17 +922,19 @@ void conv_tile_kernel(ConvArgs a) {
       issue(c4);
       read_frags(b1, fb);
       mma(fa);
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PI + 2), 0);  // DS read
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      for (int q = 0; q < 2 * CPS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MPS / (2 * CPS), 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
       }
+      if constexpr (MPS % (2 * CPS) != 0)
+        __builtin_amdgcn_sched_group_barrier(0x008, MPS % (2 * CPS), 0);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(b2, fa);
       mma(fb);
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PI + 2), 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0);  // MFMA
       __builtin_amdgcn_sched_barrier(0);
     };
     for (; st + 4 <= nst; st += 4) {
@@ -958,9 +972,9 @@ void conv_tile_kernel(ConvArgs a) {
       cis_l[e] = a.cis_vec ? eb[256 + cl + e] : a.cis;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = wm * 64 + i * 16 + col;
-      const int m = blockIdx.x * kTileBM + p;
+    for (int i = 0; i < PI; ++i) {
+      const int p = wm * (BM / 2) + i * 16 + col;
+      const int m = blockIdx.x * BM + p;
       if (m >= a.M) continue;
       int32_t v[8];
 #pragma unroll
@@ -986,8 +1000,8 @@ void conv_tile_kernel(ConvArgs a) {
       fpar.beta[e] = a.use_bn ? ep[1024 + e] : 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = blockIdx.x * kTileBM + wm * 64 + i * 16 + col;
+    for (int i = 0; i < PI; ++i) {
+      const int m = blockIdx.x * BM + wm * (BM / 2) + i * 16 + col;
       if (m >= a.M) continue;
       float v[8];
 #pragma unroll
@@ -1906,10 +1920,21 @@ hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   // one 128-channel tile (K <= 128: 4% on the CBNA 5x5 and 7x7 layers, equal
   // on the strided int8 layer); one per stage otherwise (3% slower with two
   // on the 256-channel bf16 layer).
-  if (p->d.K <= kTileBN)
-    hipLaunchKernelGGL((conv_tile_kernel<DT, true, true>), grid, dim3(kTileThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((conv_tile_kernel<DT, true, false>), grid, dim3(kTileThreads), 0, s, a);
+  // 64-pixel tiles where 128-pixel ones would leave at least half the CUs
+  // idle (the CBNA layers: 98 tiles), unless the plan pins the height.
+  const int64_t tiles = static_cast<int64_t>(grid.x) * grid.y;
+  const bool bm64 = p->pixel_tiles == 1 || (p->pixel_tiles == 0 && tiles * 2 <= device_cu_count());
+  if (bm64) {
+    const dim3 grid64(static_cast<unsigned>((p->M + 63) / 64), grid.y);
+    if (p->d.K <= kTileBN)
+      hipLaunchKernelGGL((conv_tile_kernel<DT, true, true, 64>), grid64, dim3(kTileThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((conv_tile_kernel<DT, true, false, 64>), grid64, dim3(kTileThreads), 0, s, a);
+  } else if (p->d.K <= kTileBN) {
+    hipLaunchKernelGGL((conv_tile_kernel<DT, true, true, 128>), grid, dim3(kTileThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((conv_tile_kernel<DT, true, false, 128>), grid, dim3(kTileThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

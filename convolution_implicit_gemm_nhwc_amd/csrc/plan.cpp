@@ -78,7 +78,8 @@ constexpr int64_t kRfMaxLds = 80 * 1024;
 // Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream (environment)
 // pins a kernel family where the shape allows it, for A/B comparisons;
 // FCONV_RF_PT=1|2|4 overrides the pixel tiles, FCONV_HALO_ROWS the output rows
-// per workgroup of the row-halo kernel.
+// per workgroup of the row-halo kernel, FCONV_TILE_BM=64|128 the pixel rows
+// of the tiled kernel's tile (otherwise chosen at launch from the grid size).
 void choose_variant(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
   p->variant = kGeneral;
@@ -100,6 +101,10 @@ void choose_variant(fconv_plan_s* p) {
   if (!force_general && !force_rf && p->load_mode == kLoadTap && d.K % 16 == 0 && sizes_ok &&
       tile_ok && (ksteps > 9 || rf_lds > kRfMaxLds || force_tile)) {
     p->variant = kTiled;
+    p->pixel_tiles = 0;
+    const char* bm = getenv("FCONV_TILE_BM");
+    if (bm && atoi(bm) == 64) p->pixel_tiles = 1;
+    if (bm && atoi(bm) == 128) p->pixel_tiles = 2;
   } else if (!force_general && p->load_mode == kLoadTap && d.K % 16 == 0 && rf_lds <= kRfMaxLds &&
       sizes_ok) {
     p->variant = kResidentFilter;
@@ -228,7 +233,11 @@ int list_configs(const fconv_plan_s* p, KernelConfig* out, int max) {
   const FamilyFit f = family_fit(p);
   if (f.halo) add(kHalo, 1, 0, 0);
   if (f.stream) add(kStream, 1, 0, 0);
-  if (f.tile) add(kTiled, 1, 0, 0);
+  if (f.tile) {
+    add(kTiled, 0, 0, 0);
+    add(kTiled, 1, 0, 0);
+    add(kTiled, 2, 0, 0);
+  }
   if (f.rf) {
     static const int32_t pt_rd[6][2] = {{1, 4}, {1, 9}, {2, 4}, {2, 9}, {4, 2}, {4, 4}};
     for (const auto& c : pt_rd) add(kResidentFilter, c[0], c[1], 0);
