@@ -52,6 +52,32 @@ def _addr(t):
     return t.data_ptr()
 
 
+_TORCH_DTYPES = {"int8": ("torch.int8",), "bf16": ("torch.bfloat16",),
+                 "fp32": ("torch.float32",)}
+
+
+def _validate(checks):
+    """Checks every (tensor, name, numel, dtypes) against what the plan
+    expects: at least `numel` elements of one of `dtypes` (torch dtype
+    names).  The kernels size their reads and writes from the plan, not from
+    the allocation, so a short or mistyped tensor is rejected here, before
+    any device address is taken or the C ABI is called (a longer one is
+    safe: only its first `numel` elements are touched).  None is skipped; an
+    int is a raw device address, which the caller vouches for."""
+    for t, what, numel, dtypes in checks:
+        if t is None or isinstance(t, int):
+            continue
+        if str(t.dtype) not in dtypes:
+            raise ValueError("%s: dtype %s, expected %s" % (what, t.dtype, " or ".join(dtypes)))
+        if t.numel() < numel:
+            raise ValueError("%s: %d elements, the plan needs %d" % (what, t.numel(), numel))
+
+
+def _nbytes(t, default):
+    """Byte size of a workspace tensor (a raw address: `default`)."""
+    return t.numel() * t.element_size() if hasattr(t, "numel") else default
+
+
 def _stream_handle(stream):
     if stream is None:
         import torch
@@ -109,27 +135,39 @@ class Plan:
         return self._h
 
     def pack_filter(self, w, workspace, stream=None):
+        d = self.desc
+        _validate([(w, "w", d.R * d.S * d.C * d.K, _TORCH_DTYPES[self.dtype])])
         _check(_abi.lib().fconv_plan_pack_filter(
             self._h, _stream_handle(stream), _addr(w), _addr(workspace),
-            self.workspace_bytes if not isinstance(workspace, int) else self.workspace_bytes),
+            _nbytes(workspace, self.workspace_bytes)),
             "fconv_plan_pack_filter")
 
     def make_args(self, x, w, y, workspace, bias=None, side=None, conv_input_scale=1.0,
                   side_input_scale=0.0, bn=None, prepacked=False, workspace_bytes=None,
                   activ_alpha=0.0, activ_beta=0.0):
+        d = self.desc
+        K = d.K
+        dt = _TORCH_DTYPES[self.dtype]
+        f32 = ("torch.float32",)
+        n_out = self.out_shape[0] * self.out_shape[1] * self.out_shape[2] * K
+        cis_vec = conv_input_scale if hasattr(conv_input_scale, "data_ptr") else None
+        checks = [(x, "x", d.N * d.H * d.W * d.C, dt), (w, "w", d.R * d.S * d.C * K, dt),
+                  (y, "y", n_out, dt), (bias, "bias", K, f32),
+                  (side, "side", n_out, ("torch.int8",)),
+                  (cis_vec, "conv_input_scale", K, f32)]
+        if bn is not None:
+            checks += [(bn[k], "bn " + k, K, f32) for k in ("gamma", "beta", "mean", "var")]
+        _validate(checks)
         a = _abi.FconvArgs()
         a.x, a.w, a.y = _addr(x), _addr(w), _addr(y)
-        a.workspace = _addr(workspace)
         if workspace_bytes is None:
-            workspace_bytes = (workspace.numel() * workspace.element_size()
-                               if hasattr(workspace, "numel") else self.workspace_bytes)
+            workspace_bytes = _nbytes(workspace, self.workspace_bytes)
+        a.workspace = _addr(workspace)
         a.workspace_bytes = workspace_bytes
         a.bias, a.side = _addr(bias), _addr(side)
-        if hasattr(conv_input_scale, "data_ptr"):
+        if cis_vec is not None:
             # One fp32 value per output channel, on the GPU.
-            if conv_input_scale.numel() != self.desc.K or str(conv_input_scale.dtype) != "torch.float32":
-                raise ValueError("a conv_input_scale tensor needs K fp32 values")
-            a.conv_input_scales = _addr(conv_input_scale)
+            a.conv_input_scales = _addr(cis_vec)
             a.conv_input_scale = 0.0
         else:
             a.conv_input_scale = conv_input_scale
@@ -219,8 +257,12 @@ class WgradPlan:
     def run_raw(self, x, dy, dw, workspace, workspace_bytes=None, stream=None) -> int:
         """Enqueue; returns the raw status (no exception)."""
         if workspace_bytes is None:
-            workspace_bytes = (workspace.numel() * workspace.element_size()
-                               if hasattr(workspace, "numel") else self.workspace_bytes)
+            workspace_bytes = _nbytes(workspace, self.workspace_bytes)
+        d = self.desc
+        dt = _TORCH_DTYPES[self.dtype]
+        _validate([(x, "x", d.N * d.H * d.W * d.C, dt),
+                   (dy, "dy", d.N * self.Ho * self.Wo * d.K, dt),
+                   (dw, "dw", d.R * d.S * d.C * d.K, _TORCH_DTYPES[self.out_dtype])])
         ptrs = (_addr(x), _addr(dy), _addr(dw), _addr(workspace))
         return _abi.lib().fconv_wgrad_plan_run(self._h, _stream_handle(stream), *ptrs,
                                                workspace_bytes)

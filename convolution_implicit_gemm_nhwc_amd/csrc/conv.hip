@@ -39,6 +39,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "plan.h"
@@ -1807,18 +1808,21 @@ hipError_t launch_rf(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
   }
 }
 
+// Compute units of the current device, queried once per device.  Runs on
+// several host threads at once are allowed, so the cache entries are atomics:
+// two threads may both query a device the first time and store the same value.
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int R, int S, int CS>
@@ -2084,8 +2088,10 @@ fconv_status fconv_plan_autotune(fconv_plan p, void* stream, const fconv_args* a
     return FCONV_ERR_DEVICE;
   }
   // Agreement with the plan's own configuration (the first candidate):
-  // bit-exact for int8, the float tolerances otherwise.
-  const double tol = p->d.dtype == FCONV_INT8 ? 0.0 : p->d.dtype == FCONV_BF16 ? 2e-2 : 1e-5;
+  // bit-exact for int8.  Float configurations differ only in the order of
+  // their fp32 sums: for bf16 output that flips at most an ulp or two of the
+  // rounded result (2^-8 relative each), so 8e-3 normwise; fp32 1e-5.
+  const double tol = p->d.dtype == FCONV_INT8 ? 0.0 : p->d.dtype == FCONV_BF16 ? 8e-3 : 1e-5;
   float best = -1.0f;
   int best_i = 0;
   st = FCONV_OK;

@@ -56,9 +56,12 @@
  *    (NULL = the default stream).
  *  - The library never allocates device memory: the caller owns every buffer,
  *    including the workspace that holds the repacked filter.
- *  - A plan is a host object, immutable after creation; concurrent runs of
- *    one plan on different streams are safe when each has its own workspace
- *    and output.
+ *  - A plan is a host object.  fconv_plan_run never modifies it, so
+ *    concurrent runs of one plan on different streams are safe when each has
+ *    its own workspace and output.  The one call that changes a plan is
+ *    fconv_plan_autotune (it replaces the plan's kernel configuration and
+ *    updates a process-wide cache); it must not overlap any other call on
+ *    the same plan.
  */
 #ifndef FCONV_H
 #define FCONV_H
@@ -228,8 +231,9 @@ FCONV_API fconv_status fconv_plan_run(fconv_plan plan, void* stream, const fconv
  * buffers `args` (checked as by fconv_plan_run; y is overwritten and holds
  * the chosen configuration's result on return).  A candidate whose output
  * differs from the plan's own configuration (int8: any bit; bf16: normwise
- * 2e-2; fp32: 1e-5) is not chosen.  The fastest becomes the plan's
- * configuration and is cached for the process: later fconv_plan_create calls
+ * 8e-3, about two ulps of the rounded output; fp32: 1e-5) is not chosen.
+ * The fastest becomes the plan's configuration (the plan is modified) and is
+ * cached for the process: later fconv_plan_create calls
  * with the same descriptor start from it (unless FCONV_FORCE_VARIANT pins a
  * family).  Synchronous: returns after the stream has drained.  Must not
  * run concurrently with other calls on the same plan.  *best_us (may be

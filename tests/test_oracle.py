@@ -395,6 +395,41 @@ def test_epilogue_against_exact_rational_model():
             np.testing.assert_array_equal(y, np.array(exp, np.int8))
 
 
+def test_epilogue_large_accumulators_against_exact_rational_model():
+    """Accumulators between 2^24 and 2^31, where the int32 -> fp32 conversion
+    rounds (odd values above 2^24 are ties), with biases that bring t back
+    into the int8 range so that every rounding step shows in the output;
+    both orders, against exact rational arithmetic rounded to binary32."""
+    rng = np.random.default_rng(16)
+    n = 3000
+    mag = rng.integers(2 ** 24, 2 ** 27, size=n)
+    mag[: n // 3] = rng.integers(2 ** 24, 2 ** 24 + 64, size=n // 3)
+    mag[n // 3: n // 2] = rng.integers(2 ** 31 - 2 ** 20, 2 ** 31, size=n // 2 - n // 3)
+    acc = (mag * rng.choice([-1, 1], size=n)).astype(np.int64)
+    acc = np.clip(acc, -2 ** 31, 2 ** 31 - 1).astype(np.int32)
+    side = wl.draw_int8(rng, (n,), -128, 127)
+    for cis in (np.float32(0.5), np.float32(1.0), np.float32(0.7), np.float32(2.0 ** -3)):
+        # bias = -(acc * cis) in fp32 plus a small offset: t lands near the
+        # int8 range, so the conversion's rounding decides the result.
+        off = rng.choice([0.0, 0.5, -0.5, 1.0, 3.25, -7.0, 100.0], size=n)
+        bias = (-(acc.astype(np.float64) * float(cis)) + off).astype(np.float32)
+        sis = np.float32(0.377)
+        for order in (7, 8):
+            for relu in (False, True):
+                for with_side in (False, True):
+                    y = oracle.epilogue_i8(acc.reshape(1, 1, 1, n), cis, bias,
+                                           side.reshape(1, 1, 1, n) if with_side else None,
+                                           sis, relu, order)
+                    # bias is per channel: one channel per value here
+                    exp = [_epilogue_exact(acc[i], cis, side[i] if with_side else None, sis,
+                                           bias[i], relu, order) for i in range(n)]
+                    np.testing.assert_array_equal(y.reshape(-1), np.array(exp, np.int8))
+    # the construction puts most outputs strictly inside the range
+    y = oracle.epilogue_i8(acc.reshape(1, 1, 1, n), np.float32(1.0),
+                           (-acc.astype(np.float64)).astype(np.float32), None, 0.0, False)
+    assert np.mean(np.abs(y.astype(int)) < 127) > 0.9
+
+
 def test_epilogue_variants_against_exact_rational_model():
     """Both orders with a per-channel scale vector: the oracle's fp32 steps
     equal exact rational arithmetic rounded to binary32 at each step (in the

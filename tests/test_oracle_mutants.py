@@ -38,6 +38,13 @@ MUTANTS = [
        "        if (use_side) t = t + bias[k];")]),
     ("round half away from zero", "void oracle_epilogue_i8_ex(",
      [("      t = nearbyintf(t);", "      t = roundf(t);")]),
+    ("int32 -> fp32 conversion truncates toward zero", "void oracle_epilogue_i8_ex(",
+     [("      float t = (float)acc[i];          /* int32 -> fp32, round to nearest even */",
+       "      float t = (float)(double)(acc[i] / (1 << (acc[i] > 16777216 || acc[i] < -16777216))"
+       " * (1 << (acc[i] > 16777216 || acc[i] < -16777216)));")]),
+    ("int32 -> fp32 conversion rounds ties up", "void oracle_epilogue_i8_ex(",
+     [("      float t = (float)acc[i];          /* int32 -> fp32, round to nearest even */",
+       "      float t = (float)((acc[i] > 16777216 && (acc[i] & 1)) ? (long)acc[i] + 1 : acc[i]);")]),
     ("clip lower bound -127", "void oracle_epilogue_i8_ex(",
      [("  const float lo = relu ? 0.0f : -128.0f;", "  const float lo = relu ? 0.0f : -127.0f;")]),
     ("SAME padding: the odd pixel before", "int oracle_geometry(",
