@@ -184,6 +184,19 @@ class Plan:
         """Enqueue with a prepared FconvArgs; returns the raw status."""
         return _abi.lib().fconv_plan_run(self._h, _stream_handle(stream), ctypes.byref(args))
 
+    def run_no_alloc_args(self, args, stream=None) -> int:
+        """fconv_plan_run_no_alloc with a prepared FconvArgs (its workspace
+        fields are ignored); returns the raw status."""
+        return _abi.lib().fconv_plan_run_no_alloc(self._h, _stream_handle(stream),
+                                                  ctypes.byref(args))
+
+    def run_no_alloc(self, x, w, y, stream=None, **kw):
+        """Run with the library's own device scratch instead of a workspace
+        (fconv_plan_run_no_alloc): nothing is allocated per call."""
+        _check(self.run_no_alloc_args(self.make_args(x, w, y, None, workspace_bytes=0, **kw),
+                                      stream), "fconv_plan_run_no_alloc")
+        return y
+
     def autotune(self, x, w, y, workspace, repeats=20, stream=None, **kw):
         """Time every kernel configuration for this shape on these buffers and
         keep the fastest (see fconv_plan_autotune); returns its microseconds

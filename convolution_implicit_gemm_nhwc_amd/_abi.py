@@ -21,6 +21,7 @@ FCONV_MAX_OPS = 8
 FCONV_RUN_FILTER_PREPACKED = 1
 FCONV_DESC_CUDNN7_ORDER = 1
 FCONV_WGRAD_OUT_FP32 = 1
+FCONV_NO_ALLOC_SCRATCH_BYTES = 4 << 20
 
 # Every symbol include/fconv.h declares.
 EXPORTS = ("fconv_plan_create", "fconv_plan_output_dims", "fconv_plan_workspace_size",
@@ -29,7 +30,7 @@ EXPORTS = ("fconv_plan_create", "fconv_plan_output_dims", "fconv_plan_workspace_
            "fconv_autotune_cache_clear", "fconv_wgrad_plan_create",
            "fconv_wgrad_plan_output_dims", "fconv_wgrad_plan_workspace_size",
            "fconv_wgrad_plan_run", "fconv_wgrad_plan_kernel_name",
-           "fconv_wgrad_plan_destroy")
+           "fconv_wgrad_plan_destroy", "fconv_plan_run_no_alloc")
 
 
 class FconvDesc(ctypes.Structure):
@@ -82,6 +83,8 @@ def lib():
         L.fconv_plan_pack_filter.restype = st
         L.fconv_plan_run.argtypes = [P, P, ctypes.POINTER(FconvArgs)]
         L.fconv_plan_run.restype = st
+        L.fconv_plan_run_no_alloc.argtypes = [P, P, ctypes.POINTER(FconvArgs)]
+        L.fconv_plan_run_no_alloc.restype = st
         L.fconv_plan_destroy.argtypes = [P]
         L.fconv_plan_destroy.restype = st
         L.fconv_plan_kernel_name.argtypes = [P]

@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "plan.h"
@@ -2041,6 +2042,44 @@ double output_difference(const fconv_plan_s* p, const std::vector<uint8_t>& a,
 }  // namespace
 }  // namespace fconv
 
+// ---------------------------------------------- runs that allocate nothing
+//
+// fconv_plan_run_no_alloc keeps the run's scratch (the repacked filter) in
+// this file-scope device array instead of a caller workspace.  Each device
+// holds its own copy at its own address until the process ends; host code
+// reaches it only through the per-device address hipGetSymbolAddress
+// returns (the array's name is a host-side stand-in, not a device address).
+constexpr size_t kNoAllocScratchBytes = FCONV_NO_ALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace fconv {
+namespace {
+
+// Device address of `scratch` on device `dev`, looked up once per device with
+// that device current; nullptr if the runtime reports an error.
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev]) return addr[dev];
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  addr[dev] = ptr;
+  return ptr;
+}
+
+}  // namespace
+}  // namespace fconv
+
 extern "C" {
 
 fconv_status fconv_plan_pack_filter(fconv_plan p, void* stream, const void* w,
@@ -2065,6 +2104,23 @@ fconv_status fconv_plan_run(fconv_plan p, void* stream, const fconv_args* args) 
   return FCONV_OK;
 }
 
+
+fconv_status fconv_plan_run_no_alloc(fconv_plan p, void* stream, const fconv_args* args) {
+  if (!p || !args) return FCONV_ERR_INVALID_ARG;
+  if (p->ws_bytes > kNoAllocScratchBytes) return FCONV_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) {
+    (void)hipGetLastError();
+    return FCONV_ERR_DEVICE;
+  }
+  void* ws = fconv::scratch_address(dev);
+  if (!ws) return FCONV_ERR_DEVICE;
+  fconv_args a = *args;
+  a.workspace = ws;
+  a.workspace_bytes = kNoAllocScratchBytes;
+  return fconv_plan_run(p, stream, &a);
+}
 
 fconv_status fconv_plan_autotune(fconv_plan p, void* stream, const fconv_args* args,
                                  int32_t repeats, float* best_us) {

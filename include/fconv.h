@@ -223,6 +223,24 @@ FCONV_API fconv_status fconv_plan_pack_filter(fconv_plan plan, void* stream, con
  * FCONV_ERR_DEVICE (launch failure). */
 FCONV_API fconv_status fconv_plan_run(fconv_plan plan, void* stream, const fconv_args* args);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * run as fconv_plan_run, with args->workspace and args->workspace_bytes
+ * ignored.  The run's scratch (the repacked filter) lives in a device array
+ * of FCONV_NO_ALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; nothing is allocated or freed per call.  Every
+ * call on one GPU shares that GPU's array and leaves the last call's contents
+ * in it, so calls that overlap on one GPU (other streams, other threads)
+ * race; FCONV_RUN_FILTER_PREPACKED reuses the filter the previous call on
+ * that GPU packed, and is only meaningful when that call had a plan with the
+ * same C, K, R, S and dtype and the same filter.  Errors: as fconv_plan_run;
+ * FCONV_ERR_WORKSPACE when the plan's workspace size exceeds
+ * FCONV_NO_ALLOC_SCRATCH_BYTES; FCONV_ERR_DEVICE when the array's device
+ * address cannot be obtained. */
+#define FCONV_NO_ALLOC_SCRATCH_BYTES (4u << 20)
+FCONV_API fconv_status fconv_plan_run_no_alloc(fconv_plan plan, void* stream,
+                                               const fconv_args* args);
+
 /* Autotuning, as TensorFlow (conv_ops_fused_int8.cc, the autotune path of
  * LaunchFusedConv2DOpGpuInt8Helper) and MXNet (cudnn_deconvolution-inl.h,
  * SelectAlgo) pick among algorithms by timing them and caching the choice per
