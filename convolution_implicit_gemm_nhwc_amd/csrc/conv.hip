@@ -41,6 +41,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "plan.h"
@@ -132,6 +133,10 @@ struct ConvArgs {
   // Row-halo kernel: output rows per workgroup and rows of its first phase
   // (set by its launcher).
   int32_t halo_rows, halo_rows_a;
+  // Full-size VALID GEMM: partial sums [gemm_splits][N][Kp] (4 bytes each) in
+  // the workspace after the packed filter, k-steps per split, padded K.
+  void* part;
+  int32_t gemm_splits, gemm_kps, Kp;
 };
 
 // ------------------------------------------------------------ filter repack
@@ -253,9 +258,9 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
   }
   if (kvec) {
     if constexpr (NCH == 16)
-      *reinterpret_cast<i32x4*>(y) = o.v;
+      __builtin_nontemporal_store(o.v, reinterpret_cast<i32x4*>(y));
     else
-      *reinterpret_cast<i32x2*>(y) = i32x2{o.v.x, o.v.y};
+      __builtin_nontemporal_store(i32x2{o.v.x, o.v.y}, reinterpret_cast<i32x2*>(y));
   } else {
 #pragma unroll
     for (int e = 0; e < NCH; ++e)
@@ -334,7 +339,8 @@ __device__ inline void epilogue_store_float(const float (&v)[NCH], const ConvArg
     for (int e = 0; e < NCH; ++e) o.h[e] = f32_to_bf16_rne(t[e]);
     if (kvec) {
 #pragma unroll
-      for (int q = 0; q < NCH / 8; ++q) reinterpret_cast<i32x4*>(y)[q] = o.v[q];
+      for (int q = 0; q < NCH / 8; ++q)
+        __builtin_nontemporal_store(o.v[q], reinterpret_cast<i32x4*>(y) + q);
     } else {
 #pragma unroll
       for (int e = 0; e < NCH; ++e)
@@ -1049,6 +1055,12 @@ __device__ inline uint32_t pack_word(uint32_t lo_pair, uint32_t hi_pair) {
   return __builtin_amdgcn_perm(hi_pair, lo_pair, 0x05040100u);  // [lo.b0, lo.b1, hi.b0, hi.b1]
 }
 
+// Cache policy of int8 and bf16 output stores: non-temporal.  y is written
+// once and never read back by the kernel; streaming it out instead of leaving
+// it resident in L2 measured 0.3 us faster on the 3x3 int8 layer and 0.55 us
+// on the 1x1 (the fp32 stores of the tiled kernel were 1% slower with it).
+constexpr int kStoreNT = 2;
+
 // One lane's NOUT/4 packed output words with a single buffer store.
 template <int NOUT>
 __device__ inline void store_words(const uint32_t (&w)[NOUT / 4], __amdgpu_buffer_rsrc_t yr,
@@ -1057,10 +1069,10 @@ __device__ inline void store_words(const uint32_t (&w)[NOUT / 4], __amdgpu_buffe
     __builtin_amdgcn_raw_buffer_store_b128(
         i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]),
               static_cast<int32_t>(w[2]), static_cast<int32_t>(w[3])},
-        yr, off, 0, 0);
+        yr, off, 0, kStoreNT);
   else
     __builtin_amdgcn_raw_buffer_store_b64(
-        i32x2{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1])}, yr, off, 0, 0);
+        i32x2{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1])}, yr, off, 0, kStoreNT);
 }
 
 // Requantisation of a lane's NOUT (8 or 16) outputs, organised by stage so
@@ -1750,6 +1762,172 @@ void conv_halo_i8_kernel(ConvArgs a) {
   }
 }
 
+// ------------------------------------------------- full-size VALID as a GEMM
+//
+// A filter as large as the image with VALID padding has a single output
+// pixel per image, and the convolution is one matrix product (TensorFlow
+// conv_ops_fused_int8.cc, LaunchFusedConv2DOpCpuInt8Helper, the second GEMM
+// special case):  y[n][k] = sum_j x[n][j] * w[j][k],  j = (r, s, c) over the
+// whole image, x viewed as [N][H*W*C] and the filter as [R*S*C][K].  Both
+// operands are contiguous along j (an NHWC image; a packed filter row).
+//
+// The product is thin (N images) and deep (H*W*C), and the filter is almost
+// all of its bytes: the work is streaming the filter.  To put every CU on
+// it, the reduction is split into ranges: a workgroup owns 32 output
+// channels, 32 images and one range (grid: channel tiles x ranges x image
+// tiles).  Its 16 waves each stream a contiguous part of the range with
+// fragments loaded straight from global memory into registers (x, re-read
+// by every channel tile, stays in L2), four k-steps of loads in flight, and
+// add their 32 x 32 partial sums through LDS in wave order.  The workgroup
+// writes its partial tile [range][n][k] (int32 for int8, fp32 otherwise) to
+// the workspace.  A second kernel adds the ranges in range order and runs
+// the fused epilogue, so every run gives the same bits.  (Adding the ranges
+// in the last workgroup of each tile instead needs a device-scope release
+// per workgroup, an L2 write-back each: measured 10x slower.)  Requires
+// R*S*C*esize to be whole 64-byte k-steps.
+constexpr int kGemmWaves = 16;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+constexpr int kGemmBN = 32;    // output channels per workgroup (half a packed 64-row block)
+constexpr int kGemmBatch = 4;  // k-steps of loads in flight per wave
+
+template <int DT>
+__global__ __launch_bounds__(kGemmThreads) void conv_gemm_splitk_kernel(ConvArgs a) {
+  using Acc = typename Dt<DT>::Acc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int g = lane >> 4, col = lane & 15;
+  const int ct = blockIdx.x, split = blockIdx.y, nt = blockIdx.z, n0 = nt * 32;
+  const int row_bytes = a.Kg * (16 / Dt<DT>::kChunk);  // bytes of one image / filter row
+  const int nks = row_bytes >> 6;                      // 64-byte k-steps
+  // This workgroup's k-steps [kb, ke), and this wave's contiguous part.
+  const int kb = split * a.gemm_kps;
+  const int ke = min(kb + a.gemm_kps, nks);
+  const int per_wave = (a.gemm_kps + kGemmWaves - 1) / kGemmWaves;
+  const int wb = kb + wave * per_wave;
+  const int we = min(wb + per_wave, ke);
+  // Packed rows 32ct + 16jj + col (jj = 0, 1) hold, for lane group g, the
+  // channels chb(g) + 4jj .. +3 with chb(g) = 64(ct/2) + 16g + 8(ct%2): eight
+  // consecutive channels per lane (the repack's order inside a 64-row block).
+  const int chb = 64 * (ct >> 1) + 8 * (ct & 1);
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+  uint32_t xo[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = n0 + 16 * i + col;
+    xo[i] = n < a.N ? static_cast<uint32_t>(n * row_bytes + 16 * g) : kOutOfRange;
+  }
+  const uint32_t wo = static_cast<uint32_t>((kGemmBN * ct + col) * a.wrow_bytes + 16 * g);
+
+  Acc acc[2][2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[jj][i] = Acc{0, 0, 0, 0};
+  for (int k0 = wb; k0 < we; k0 += kGemmBatch) {
+    i32x4 fa[kGemmBatch][2], fb[kGemmBatch][2];
+#pragma unroll
+    for (int b = 0; b < kGemmBatch; ++b) {
+      const bool live = k0 + b < we;
+      const uint32_t kbyte = static_cast<uint32_t>((k0 + b) * 64);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        fa[b][jj] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, live ? wo + static_cast<uint32_t>(16 * jj * a.wrow_bytes) + kbyte : kOutOfRange,
+            0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fb[b][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, live && xo[i] != kOutOfRange ? xo[i] + kbyte : kOutOfRange, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < kGemmBatch; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[jj][i] = mma_chunk(fa[b][jj], fb[b][i], acc[jj][i], static_cast<Dt<DT>*>(nullptr));
+  }
+
+  // The waves' tiles, added through LDS in wave order: slot q = 2jj + i of
+  // wave w holds lane l's four values at ((w * 4 + q) * 64 + l) * 16.
+  __shared__ __attribute__((aligned(16))) char red[kGemmWaves * 4 * 1024];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<Acc*>(red + ((wave * 4 + 2 * jj + i) * 64 + lane) * 16) = acc[jj][i];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int64_t tile_stride = static_cast<int64_t>(a.N) * a.Kp * 4;  // bytes of one range's tiles
+  char* part = static_cast<char*>(a.part);
+  if (t < 256) {
+    // Thread t: slot q = t / 64 of lane l = t % 64, i.e. channels
+    // chb(l / 16) + 4jj .. +3 of image n0 + 16i + l % 16.
+    const int q = t >> 6, l = t & 63;
+    Acc sum = *reinterpret_cast<const Acc*>(red + (q * 64 + l) * 16);
+#pragma unroll
+    for (int w = 1; w < kGemmWaves; ++w)
+      sum = sum + *reinterpret_cast<const Acc*>(red + ((w * 4 + q) * 64 + l) * 16);
+    const int n = n0 + 16 * (q & 1) + (l & 15);
+    const int ch = chb + 16 * (l >> 4) + 4 * (q >> 1);
+    if (n < a.N)
+      *reinterpret_cast<Acc*>(part + split * tile_stride + (static_cast<int64_t>(n) * a.Kp + ch) * 4) =
+          sum;
+  }
+}
+
+// Sum of the ranges (in range order) and the fused epilogue: thread =
+// 8 consecutive channels of one image; workgroups of one wave, so the sum's
+// reads spread over many CUs.  The partial tiles are read eight ranges at a
+// time (all eight loads in flight), then added in range order.
+constexpr int kGemmReduceThreads = 64;
+
+template <int DT, bool KVEC>
+__global__ __launch_bounds__(kGemmReduceThreads) void conv_gemm_reduce_kernel(ConvArgs a) {
+  using Acc = typename Dt<DT>::Acc;
+  using Elem = typename std::conditional<DT == FCONV_INT8, int32_t, float>::type;
+  const int groups = a.Kp >> 3;
+  const int id = blockIdx.x * kGemmReduceThreads + threadIdx.x;
+  if (id >= a.N * groups) return;
+  const int n = id / groups, ch0 = (id - n * groups) * 8;
+  if (ch0 >= a.K) return;
+  const int64_t tile_stride = static_cast<int64_t>(a.N) * a.Kp * 4;  // bytes of one range's tiles
+  const char* src = static_cast<const char*>(a.part) + (static_cast<int64_t>(n) * a.Kp + ch0) * 4;
+  Acc s0 = Acc{0, 0, 0, 0}, s1 = Acc{0, 0, 0, 0};
+  for (int sp0 = 0; sp0 < a.gemm_splits; sp0 += 8) {
+    Acc v0[8], v1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (sp0 + u < a.gemm_splits) {
+        const char* q = src + (sp0 + u) * tile_stride;
+        v0[u] = *reinterpret_cast<const Acc*>(q);
+        v1[u] = *reinterpret_cast<const Acc*>(q + 16);
+      } else {
+        v0[u] = v1[u] = Acc{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s0 = s0 + v0[u];
+      s1 = s1 + v1[u];
+    }
+  }
+  Elem v[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = s0[e];
+    v[4 + e] = s1[e];
+  }
+  if constexpr (DT == FCONV_INT8) {
+    const i32x4 sc = a.use_side ? load_side_chunk<8>(a, n, ch0, KVEC) : i32x4{0, 0, 0, 0};
+    epilogue_store_i8<8>(v, a, n, ch0, KVEC, sc);
+  } else {
+    epilogue_store_float<DT, 8>(v, a, n, ch0, KVEC);
+  }
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <int DT>
@@ -1943,7 +2121,31 @@ hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   return hipGetLastError();
 }
 
+template <int DT>
+hipError_t launch_gemm(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p->Kp / kGemmBN), static_cast<unsigned>(p->gemm_splits),
+                  static_cast<unsigned>((p->d.N + 31) / 32));
+  hipLaunchKernelGGL(conv_gemm_splitk_kernel<DT>, grid, dim3(kGemmThreads), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = static_cast<int64_t>(p->d.N) * (p->Kp / 8);
+  const dim3 g2(static_cast<unsigned>((threads + kGemmReduceThreads - 1) / kGemmReduceThreads));
+  if (p->d.K % 8 == 0)
+    hipLaunchKernelGGL((conv_gemm_reduce_kernel<DT, true>), g2, dim3(kGemmReduceThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_gemm_reduce_kernel<DT, false>), g2, dim3(kGemmReduceThreads), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {
+  if (p->variant == kGemm) {
+    switch (p->d.dtype) {
+      case FCONV_INT8: return launch_gemm<FCONV_INT8>(p, a, s);
+      case FCONV_BF16: return launch_gemm<FCONV_BF16>(p, a, s);
+      default: return launch_gemm<FCONV_FP32>(p, a, s);
+    }
+  }
   if (p->variant == kStream) return launch_stream(p, a, s);
   if (p->variant == kHalo) return launch_halo(p, a, s);
   if (p->variant == kTiled) {
@@ -2000,7 +2202,11 @@ ConvArgs make_conv_args(const fconv_plan_s* p, const fconv_args* args) {
   a.x_bytes = static_cast<uint32_t>(p->x_elems * p->esize);
   a.y_bytes = static_cast<uint32_t>(p->y_elems * p->esize);
   a.side_bytes = static_cast<uint32_t>(p->y_elems);
-  a.wp_bytes = static_cast<uint32_t>(p->ws_bytes);
+  a.wp_bytes = static_cast<uint32_t>(p->pack_bytes);
+  a.part = p->part_offset ? static_cast<char*>(args->workspace) + p->part_offset : nullptr;
+  a.gemm_splits = p->gemm_splits;
+  a.gemm_kps = p->gemm_kps;
+  a.Kp = p->Kp;
   a.tiles = static_cast<int32_t>((p->M + 15) / 16);
   a.wo_mul = p->wo_div.mul; a.wo_add = p->wo_div.add; a.wo_shift = p->wo_div.shift;
   a.ho_mul = p->ho_div.mul; a.ho_add = p->ho_div.add; a.ho_shift = p->ho_div.shift;

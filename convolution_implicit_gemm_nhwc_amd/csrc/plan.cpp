@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <new>
@@ -62,21 +63,35 @@ fconv_status parse_ops(fconv_plan_s* p) {
 }
 
 const char* kernel_name(int32_t variant, int32_t dtype) {
-  static const char* names[5][3] = {
+  static const char* names[6][3] = {
       {"conv_general_i8", "conv_general_bf16", "conv_general_f32"},
       {"conv_rf_i8", "conv_rf_bf16", "conv_rf_f32"},
       {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"},
       {"conv_tile_i8", "conv_tile_bf16", "conv_tile_f32"},
-      {"conv_halo_i8", "conv_halo_bf16", "conv_halo_f32"}};
+      {"conv_halo_i8", "conv_halo_bf16", "conv_halo_f32"},
+      {"conv_gemm_i8", "conv_gemm_bf16", "conv_gemm_f32"}};
   return names[variant][dtype];
+}
+
+// A filter as large as the image with VALID padding (one output pixel per
+// image: the GEMM special case of the fused op), whose image rows are whole
+// 64-byte k-steps, in 32-bit buffer extents.
+bool gemm_shape(const fconv_plan_s* p) {
+  const fconv_desc& d = p->d;
+  return d.padding == FCONV_PAD_VALID && d.R == d.H && d.S == d.W &&
+         (static_cast<int64_t>(p->Kg) * p->esize) % 64 == 0 &&
+         p->x_elems * p->esize < (int64_t{1} << 31) &&
+         static_cast<int64_t>(p->pack_bytes) < (int64_t{1} << 31);
 }
 
 // LDS budget of the resident-filter kernel's 64-row filter slice: at most
 // this much, so that two workgroups still fit in a CU's 160 KiB.
 constexpr int64_t kRfMaxLds = 80 * 1024;
 
-// Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream (environment)
-// pins a kernel family where the shape allows it, for A/B comparisons;
+// Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream|gemm
+// (environment) pins a kernel family where the shape allows it, for A/B
+// comparisons (a full-size VALID filter takes the GEMM kernel unless another
+// family is pinned);
 // FCONV_RF_PT=1|2|4 overrides the pixel tiles, FCONV_HALO_ROWS the output rows
 // per workgroup of the row-halo kernel, FCONV_TILE_BM=64|128 the pixel rows
 // of the tiled kernel's tile (otherwise chosen at launch from the grid size).
@@ -86,13 +101,19 @@ void choose_variant(fconv_plan_s* p) {
   p->pixel_tiles = 1;
   p->ring_depth = 0;
   p->halo_rows = 0;
+  const char* force0 = getenv("FCONV_FORCE_VARIANT");
+  if (gemm_shape(p) && (!force0 || strcmp(force0, "gemm") == 0)) {
+    p->variant = kGemm;
+    p->kernel_name = kernel_name(p->variant, d.dtype);
+    return;
+  }
   const int64_t rf_lds = 64 * static_cast<int64_t>(p->wrow_bytes);
   const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
   const char* force = getenv("FCONV_FORCE_VARIANT");
   const bool force_general = force && strcmp(force, "general") == 0;
   const bool force_tile = force && strcmp(force, "tile") == 0;
   const bool sizes_ok = x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31) &&
-                        static_cast<int64_t>(p->ws_bytes) < (int64_t{1} << 31);
+                        static_cast<int64_t>(p->pack_bytes) < (int64_t{1} << 31);
   // Long tap-aligned reductions (more than 9 k-steps of 64 bytes) whose
   // channels fill whole 128-byte stages: the LDS-tiled kernel.
   const bool force_rf = force && strcmp(force, "rf") == 0;
@@ -152,7 +173,7 @@ void choose_variant(fconv_plan_s* p) {
 
 // Shape conditions of each family, as choose_variant applies them.
 struct FamilyFit {
-  bool rf, tile, stream, halo;
+  bool rf, tile, stream, halo, gemm;
 };
 
 FamilyFit family_fit(const fconv_plan_s* p) {
@@ -160,7 +181,7 @@ FamilyFit family_fit(const fconv_plan_s* p) {
   const int64_t rf_lds = 64 * static_cast<int64_t>(p->wrow_bytes);
   const int64_t x_bytes = p->x_elems * p->esize, y_bytes = p->y_elems * p->esize;
   const bool sizes_ok = x_bytes < (int64_t{1} << 31) && y_bytes < (int64_t{1} << 31) &&
-                        static_cast<int64_t>(p->ws_bytes) < (int64_t{1} << 31);
+                        static_cast<int64_t>(p->pack_bytes) < (int64_t{1} << 31);
   FamilyFit f;
   const bool tap = p->load_mode == kLoadTap && d.K % 16 == 0 && sizes_ok;
   f.tile = tap && (static_cast<int64_t>(d.C) * p->esize) % 128 == 0;
@@ -172,6 +193,7 @@ FamilyFit family_fit(const fconv_plan_s* p) {
   f.stream = f.rf && d.dtype == FCONV_INT8 && shape_ok && tiles * 1024 < (int64_t{1} << 31);
   f.halo = f.stream && d.R == 3 && d.S == 3 && cs == 1 && d.stride_h == 1 && d.stride_w == 1 &&
            d.W + p->pl + p->pr <= 64;
+  f.gemm = gemm_shape(p);
   return f;
 }
 
@@ -231,6 +253,7 @@ int list_configs(const fconv_plan_s* p, KernelConfig* out, int max) {
   };
   add(p->variant, p->pixel_tiles, p->ring_depth, p->halo_rows);
   const FamilyFit f = family_fit(p);
+  if (f.gemm) add(kGemm, 0, 0, 0);
   if (f.halo) add(kHalo, 1, 0, 0);
   if (f.stream) add(kStream, 1, 0, 0);
   if (f.tile) {
@@ -395,7 +418,23 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
   p->KgP = static_cast<int32_t>(kgp);
   p->Kp = static_cast<int32_t>(kp);
   p->wrow_bytes = static_cast<int32_t>(kgp * p->esize + 16);
-  p->ws_bytes = static_cast<size_t>(kp * p->wrow_bytes);
+  p->pack_bytes = static_cast<size_t>(kp * p->wrow_bytes);
+  p->ws_bytes = p->pack_bytes;
+  p->part_offset = 0;
+  p->gemm_splits = p->gemm_kps = 0;
+  if (gemm_shape(p)) {
+    // Split the reduction so that 32-channel tiles x 32-image tiles x ranges
+    // come to at least one workgroup per CU (256 on the MI355X), with at
+    // least 16 k-steps (one per wave) in a range.
+    const int64_t nks = kg * p->esize / 64;
+    const int64_t tiles = (kp / 32) * ((d.N + 31) / 32);
+    int64_t splits = 1;
+    while (splits * tiles < 256 && nks / (2 * splits) >= 16) splits *= 2;
+    p->gemm_splits = static_cast<int32_t>(splits);
+    p->gemm_kps = static_cast<int32_t>((nks + splits - 1) / splits);
+    p->part_offset = static_cast<size_t>(round_up(static_cast<int64_t>(p->pack_bytes), 256));
+    p->ws_bytes = p->part_offset + static_cast<size_t>(splits) * d.N * kp * 4;
+  }
   if (d.C % kstep == 0)
     p->load_mode = kLoadTap;
   else if (d.C % p->chunk_elems == 0)

@@ -17,6 +17,7 @@ enum Variant : int32_t {
   kStream = 2,         // int8, short reduction: filter in registers, persistent
   kTiled = 3,          // 128x128 LDS-tiled implicit GEMM, long reductions
   kHalo = 4,           // int8 stride 1 over 64 channels: input rows staged in LDS
+  kGemm = 5,           // full-size VALID filter: split-reduction GEMM + sum/epilogue
 };
 
 // Division by a runtime constant d for numerators below 2^31:
@@ -62,7 +63,11 @@ struct fconv_plan_s {
   int32_t halo_rows;    // kHalo: output rows per workgroup, 0 = sized to the device
   int32_t wrow_bytes;   // packed filter row stride: KgP * esize + 16 (zero pad)
   fconv::FastDiv wo_div, ho_div;
-  size_t ws_bytes;      // packed filter: Kp * wrow_bytes
+  size_t pack_bytes;    // packed filter: Kp * wrow_bytes
+  size_t part_offset;   // kGemm-capable shapes: partial sums after the packed filter (else 0)
+  int32_t gemm_splits;  // kGemm: reduction ranges (partial tiles per output)
+  int32_t gemm_kps;     // kGemm: 64-byte k-steps per range
+  size_t ws_bytes;      // workspace: pack_bytes, then gemm_splits * N * Kp * 4 partial sums (kGemm shapes)
   int64_t x_elems, y_elems, w_elems;
   const char* kernel_name;
 };

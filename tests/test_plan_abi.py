@@ -137,8 +137,16 @@ def test_workload_plans():
         assert L.R * L.S * L.C * L.K * esize <= p.workspace_bytes
         kstep = 64 // esize
         # rows padded by one 16-byte chunk
-        assert p.workspace_bytes == (-(-L.K // 64) * 64) * (
-            -(-(L.R * L.S * L.C) // kstep) * kstep * esize + 16)
+        Kp = -(-L.K // 64) * 64
+        packed = Kp * (-(-(L.R * L.S * L.C) // kstep) * kstep * esize + 16)
+        if L.padding == "VALID" and (L.R, L.S) == (L.H, L.W):
+            # full-size filter: the split GEMM's partial sums follow the
+            # packed filter (256-byte aligned), one [N][Kp] tile per split
+            assert p.kernel_name.startswith("conv_gemm_"), p.kernel_name
+            part = p.workspace_bytes - (-(-packed // 256) * 256)
+            assert part > 0 and part % (L.N * Kp * 4) == 0
+        else:
+            assert p.workspace_bytes == packed
         assert p.kernel_name
     p = fc.Plan(64, 56, 56, 128, 128, 3, 3, 2, "SAME", "int8", INT8_OPS)
     assert p.pads == (0, 1, 0, 1)

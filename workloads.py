@@ -100,6 +100,18 @@ LAYERS = {
         "cbna_7x7s2_bf16", "bf16", N=16, H=56, W=56, C=64, K=128, R=7, S=7,
         stride=2, padding="SAME", Ho=28, Wo=28, ops=(OP_BIAS, OP_BN, OP_RELU),
         seed=6, description="N=16 56x56x64 -> 128, 7x7 s2 SAME (pads 2/3), bf16, bias+BN+ReLU"),
+    # A filter as large as the image, VALID: one output pixel per image, the
+    # GEMM special case of the fused op ([N, H*W*C] x [H*W*C, K]), shaped like
+    # a network's last 7x7x512 feature map feeding 1024 outputs.
+    "valid_7x7_int8": Layer(
+        "valid_7x7_int8", "int8", N=32, H=7, W=7, C=512, K=1024, R=7, S=7,
+        stride=1, padding="VALID", Ho=1, Wo=1, ops=(OP_SCALE, OP_BIAS, OP_RELU), seed=9,
+        x_range=(0, 127), bias_sd=16.0, conv_input_scale=2.0 ** -13,
+        description="N=32 7x7x512 -> 1024, 7x7 VALID (full-size filter), bias+ReLU"),
+    "valid_7x7_bf16": Layer(
+        "valid_7x7_bf16", "bf16", N=32, H=7, W=7, C=512, K=1024, R=7, S=7,
+        stride=1, padding="VALID", Ho=1, Wo=1, ops=(OP_BIAS, OP_BN, OP_RELU), seed=10,
+        description="N=32 7x7x512 -> 1024, 7x7 VALID (full-size filter), bf16, bias+BN+ReLU"),
 }
 
 
