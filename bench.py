@@ -85,23 +85,63 @@ def measured_traffic(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(L, inp, seconds: float, cis=None, order=8):
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _timed_oracle(L, x, w, inp, cis, order, seconds, form):
+    """Repeat the oracle's fused conv on (x, w) for about `seconds`; returns
+    the last output and the rate in TOPS of the layer's arithmetic."""
     import oracle
-    cis = L.conv_input_scale if cis is None else cis
+    n = x.shape[0]
+    side = inp.side[:n] if inp.side is not None else None
     reps, t0 = 0, time.perf_counter()
     while True:
-        acc = oracle.conv_acc(inp.x, inp.w, L.stride, L.padding)
-        y = oracle.epilogue_i8(acc, cis, inp.bias, inp.side, L.side_input_scale, L.relu,
-                               order)
+        acc = oracle.conv_acc(x, w, L.stride, L.padding, form=form)
+        y = oracle.epilogue_i8(acc, cis, inp.bias, side, L.side_input_scale, L.relu, order)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds:
             break
-    return y, dict(value=round(L.ops_count() * reps / dt / 1e12, 6), unit="TOPS",
-                   cores=oracle.num_threads(), kind="oracle",
-                   sample="full %s batch (N=%d), %d repetition(s) in %.1f s: direct "
-                          "7-loop conv + int8 epilogue, OpenMP over (n, ho)"
-                          % (L.name, L.N, reps, dt))
+    return y, reps, dt, L.ops_count() * n / L.N * reps / dt / 1e12
+
+
+def cpu_baseline(L, inp, seconds: float, cis=None, order=8):
+    """The CPU oracle timed on the host: the direct seven-loop form on all
+    cores (the headline baseline, checked against the GPU's output), on one
+    core (a bounded sample of the batch), and the im2col + GEMM form on all
+    cores."""
+    import oracle
+    cis = L.conv_input_scale if cis is None else cis
+    cores = oracle.num_threads()  # the host's OpenMP default (all the cores it grants)
+    y, reps, dt, tops = _timed_oracle(L, inp.x, inp.w, inp, cis, order, seconds, "direct")
+    out = dict(value=round(tops, 6), unit="TOPS", cores=cores, kind="oracle",
+               sample="full %s batch (N=%d), %d repetition(s) in %.1f s: direct 7-loop conv + "
+                      "int8 epilogue, OpenMP over (n, ho)" % (L.name, L.N, reps, dt),
+               cpu_model=cpu_model())
+    # One core, on the first image(s) of the batch (a bounded sample).
+    n1 = max(1, min(L.N, int(2e9 // max(1, L.ops_count() // L.N))))
+    oracle.set_num_threads(1)
+    _, r1, d1, t1 = _timed_oracle(L, inp.x[:n1], inp.w, inp, cis, order, seconds / 2, "direct")
+    out["single_thread"] = dict(value=round(t1, 6), unit="TOPS", cores=1,
+                                sample="first %d image(s), %d repetition(s) in %.1f s: direct form"
+                                       % (n1, r1, d1))
+    # The im2col + GEMM form, all cores, on the same sample size.
+    oracle.set_num_threads(cores)
+    _, r2, d2, t2 = _timed_oracle(L, inp.x[:n1], inp.w, inp, cis, order, seconds / 2, "im2col")
+    out["im2col"] = dict(value=round(t2, 6), unit="TOPS", cores=oracle.num_threads(),
+                         sample="first %d image(s), %d repetition(s) in %.1f s: per-image "
+                                "im2col patch matrix x [R*S*C, K] filter" % (n1, r2, d2))
+    return y, out
 
 
 def copy_probe(nbytes: int, steps: int, warmup: int):

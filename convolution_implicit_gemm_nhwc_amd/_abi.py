@@ -4,7 +4,11 @@ from __future__ import annotations
 import ctypes
 import os
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfconv.so")
+# FCONV_LIBRARY (environment) loads another build of the same library
+# instead, e.g. one with the host code built under address and
+# undefined-behaviour sanitizers.
+_LIB_PATH = os.environ.get("FCONV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfconv.so")
 
 FCONV_OK = 0
 FCONV_ERR_INVALID_ARG = 1

@@ -439,6 +439,24 @@ __global__ __launch_bounds__(kThreads) void conv_general_kernel(ConvArgs a) {
                                g * E;
   const int64_t tile_stride = static_cast<int64_t>(16) * (a.wrow_bytes / sizeof(T));
 
+  // The epilogue's per-channel values and side chunk are loaded before the
+  // main loop, so their latency overlaps it (on small layers the kernel is a
+  // chain of memory round trips).
+  const int ch0 = blockIdx.y * kTileN + 16 * g;
+  const bool live = mvalid && ch0 < a.K;
+  float bias[16], cis[16];
+  i32x4 sc = {0, 0, 0, 0};
+  FloatEpiParams<16> P;
+  if constexpr (DT == FCONV_INT8) {
+    if (live) {
+      load_bias<16>(a, ch0, KVEC, bias);
+      load_scales<16>(a, ch0, KVEC, cis);
+      if (a.use_side) sc = load_side_chunk(a, m, ch0, KVEC);
+    }
+  } else {
+    if (live) P.load(a, ch0, KVEC);
+  }
+
   Acc acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = Acc{0, 0, 0, 0};
@@ -465,33 +483,43 @@ __global__ __launch_bounds__(kThreads) void conv_general_kernel(ConvArgs a) {
       }
     }
   } else {
-    for (int kk = 0; kk < a.KgP; kk += KSTEP) {
-      const i32x4 b = gather_patch_chunk<DT, MODE>(xn, a, mvalid, hbase, wbase, kk + g * E);
+    // Two k-steps per trip, so that both steps' gathers are in flight at
+    // once (the second only while it lies inside the packed rows).
+    for (int kk = 0; kk < a.KgP; kk += 2 * KSTEP) {
+      const bool two = kk + KSTEP < a.KgP;  // uniform
+      const i32x4 b0 = gather_patch_chunk<DT, MODE>(xn, a, mvalid, hbase, wbase, kk + g * E);
+      const i32x4 b1 = gather_patch_chunk<DT, MODE>(xn, a, mvalid && two, hbase, wbase,
+                                                    kk + KSTEP + g * E);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const i32x4 w4 = *reinterpret_cast<const i32x4*>(wrow + j * tile_stride + kk);
-        acc[j] = mma_chunk(w4, b, acc[j], static_cast<Dt<DT>*>(nullptr));
+        acc[j] = mma_chunk(w4, b0, acc[j], static_cast<Dt<DT>*>(nullptr));
+      }
+      if (two) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const i32x4 w4 = *reinterpret_cast<const i32x4*>(wrow + j * tile_stride + kk + KSTEP);
+          acc[j] = mma_chunk(w4, b1, acc[j], static_cast<Dt<DT>*>(nullptr));
+        }
       }
     }
   }
 
-  const int ch0 = blockIdx.y * kTileN + 16 * g;
-  if (!mvalid || ch0 >= a.K) return;
+  if (!live) return;
   if constexpr (DT == FCONV_INT8) {
     int32_t v[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[4 * j + i] = acc[j][i];
-    const i32x4 sc = a.use_side ? load_side_chunk(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
-    epilogue_store_i8(v, a, m, ch0, KVEC, sc);
+    epilogue_store_i8<16>(v, a, m, ch0, KVEC, sc, bias, cis);
   } else {
     float v[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[4 * j + i] = acc[j][i];
-    epilogue_store_float<DT>(v, a, m, ch0, KVEC);
+    epilogue_store_float<DT, 16>(v, a, m, ch0, KVEC, P);
   }
 }
 

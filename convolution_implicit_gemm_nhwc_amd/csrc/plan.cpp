@@ -8,6 +8,7 @@
 // NHWC, dilation 1, BiasAdd with or without Relu) but report status codes
 // instead of aborting.
 #include <limits.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -238,6 +239,24 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// FCONV_LOG=1 (environment): one line on stderr per plan with the decisions
+// plan creation made -- geometry, padding, the kernel family and its tiling,
+// and the workspace size -- for logs and A/B comparisons.
+void log_plan(const fconv_plan_s* p, bool from_cache) {
+  const char* lg = getenv("FCONV_LOG");
+  if (!lg || !*lg || strcmp(lg, "0") == 0) return;
+  const fconv_desc& d = p->d;
+  static const char* dt[3] = {"int8", "bf16", "fp32"};
+  fprintf(stderr,
+          "fconv: plan N=%d H=%d W=%d C=%d K=%d R=%d S=%d stride=%dx%d %s %s -> Ho=%d Wo=%d "
+          "pads(t,b,l,r)=%d,%d,%d,%d kernel=%s%s pixel_tiles=%d ring_depth=%d halo_rows=%d "
+          "gemm_splits=%d workspace=%zu B\n",
+          d.N, d.H, d.W, d.C, d.K, d.R, d.S, d.stride_h, d.stride_w,
+          d.padding == FCONV_PAD_SAME ? "SAME" : "VALID", dt[d.dtype], p->Ho, p->Wo, p->pt, p->pb,
+          p->pl, p->pr, p->kernel_name, from_cache ? " (autotuned)" : "", p->pixel_tiles,
+          p->ring_depth, p->halo_rows, p->gemm_splits, p->ws_bytes);
+}
+
 }  // namespace
 
 namespace fconv {
@@ -447,7 +466,9 @@ fconv_status fconv_plan_create(const fconv_desc* desc, fconv_plan* out) {
   // A configuration autotuned earlier in this process for the same
   // descriptor wins, unless a family is pinned through the environment.
   KernelConfig cached;
-  if (!getenv("FCONV_FORCE_VARIANT") && cache_lookup(p->d, &cached)) apply_config(p, cached);
+  const bool from_cache = !getenv("FCONV_FORCE_VARIANT") && cache_lookup(p->d, &cached);
+  if (from_cache) apply_config(p, cached);
+  log_plan(p, from_cache);
   *out = p;
   return FCONV_OK;
 }
@@ -485,7 +506,11 @@ void fconv_autotune_cache_clear(void) {
 }
 
 const char* fconv_status_string(fconv_status s) {
-  switch (s) {
+  // A C caller may pass any int; reading it as the C++ enum type would be
+  // undefined for values outside the enumerators' range, so copy the bits.
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case FCONV_OK: return "ok";
     case FCONV_ERR_INVALID_ARG: return "invalid argument";
     case FCONV_ERR_UNSUPPORTED: return "unsupported";

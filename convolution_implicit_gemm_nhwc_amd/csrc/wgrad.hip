@@ -38,6 +38,7 @@
 // (blockIdx round-robins over the 8 XCDs), so the range's input and gradient
 // rows are fetched into one L2 and shared by all its tiles.
 #include <hip/hip_runtime.h>
+#include <stdio.h>
 #include <stdint.h>
 
 #include <limits.h>
@@ -974,6 +975,16 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
   p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring);
+  // FCONV_LOG=1 (environment): the plan's decisions on stderr.
+  const char* lg = getenv("FCONV_LOG");
+  if (lg && *lg && strcmp(lg, "0") != 0)
+    fprintf(stderr,
+            "fconv: wgrad plan N=%d H=%d W=%d C=%d K=%d R=%d S=%d stride=%dx%d %s %s -> Ho=%d "
+            "Wo=%d kernel=%s channel_tile=%d ring=%d pixel_ranges=%d (%d pixels each) "
+            "workspace=%zu B\n",
+            d.N, d.H, d.W, d.C, d.K, d.R, d.S, d.stride_h, d.stride_w, same ? "SAME" : "VALID",
+            d.dtype == FCONV_BF16 ? "bf16" : "fp32", p->Ho, p->Wo, p->kernel_name, p->tk, p->ring,
+            p->splits, p->m_per_split, p->ws_bytes);
   *out = p;
   return FCONV_OK;
 }

@@ -28,6 +28,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FCONV_ORACLE_LIBRARY (environment): load another build of oracle.c (e.g. one
+# built under sanitizers) instead of liboracle.so.
+_LOAD_PATH = os.environ.get("FCONV_ORACLE_LIBRARY") or _LIB_PATH
 
 CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
           "-std=c11", "-shared", "-fPIC", "-Wall"]
@@ -71,15 +74,17 @@ def _bind(lib):
     lib.oracle_wgrad_direct.argtypes = [p, p, p, p]
     lib.oracle_wgrad_direct.restype = i
     lib.oracle_num_threads.restype = i
+    lib.oracle_set_num_threads.argtypes = [i]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if _LOAD_PATH == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build(force=False)
-        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+        _lib = _bind(ctypes.CDLL(_LOAD_PATH))
     return _lib
 
 
@@ -262,3 +267,8 @@ def fused_conv_float(x, w, bias=None, bn=None, relu=False, stride=1,
 
 def num_threads():
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int):
+    """Threads of the oracle's OpenMP loops from now on (for baseline timing)."""
+    _load().oracle_set_num_threads(int(n))

@@ -457,6 +457,17 @@ void oracle_epilogue_float(const double* acc, long M, int K, const float* bias,
                            relu ? ORACLE_ACT_RELU : ORACLE_ACT_NONE, 0.0f, 0.0f, y);
 }
 
+/* Thread count of the OpenMP loops above (the baseline timing runs them on
+ * one thread and on all host cores). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
+
 int oracle_num_threads(void) {
   int n = 1;
 #pragma omp parallel

@@ -273,3 +273,27 @@ def test_autotune_checks_its_arguments():
     assert L.fconv_plan_autotune(p.handle, None, ctypes.byref(b), 5, None) == \
         _abi.FCONV_ERR_INVALID_ARG
     fc.autotune_cache_clear()
+
+
+def test_fconv_log_prints_the_plan_decisions():
+    """FCONV_LOG=1: plan creation prints its decisions (kernel family, tiling,
+    workspace) on stderr; checked in a child process so the environment
+    variable is read fresh."""
+    import subprocess
+    import sys
+    code = ("import convolution_implicit_gemm_nhwc_amd as fc\n"
+            "fc.Plan(32, 56, 56, 64, 64, 3, 3, 1, 'SAME', 'int8',"
+            " ops=('scale', 'side', 'bias', 'relu'))\n"
+            "fc.WgradPlan(2, 9, 7, 16, 24, 3, 3, 1, 'SAME', 'bf16')\n")
+    env = dict(os.environ, FCONV_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("fconv:")]
+    assert any("kernel=conv_halo_i8" in l and "Ho=56" in l and "pads(t,b,l,r)=1,1,1,1" in l
+               for l in lines), r.stderr
+    assert any(l.startswith("fconv: wgrad plan") and "kernel=wgrad_" in l for l in lines), r.stderr
+    env["FCONV_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert not [l for l in r.stderr.splitlines() if l.startswith("fconv:")]
