@@ -1511,7 +1511,57 @@ __device__ inline void wait_vmcnt_at_most(int n) {
   }
 }
 
-template <int R, int S, bool SIDE, bool ORDER7>
+// Tail of the int8 requantisation of one tile in the epilogue wave, from
+// t = (float)acc * cis (cuDNN 8 order) or t = fmaf((float)acc, cis, bias)
+// (cuDNN 7 order), which the MFMA wave computed: the side input's fused
+// multiply-add, the bias (cuDNN 8), then round half to even and clip, packed
+// into four words.  With ReLU the rounding and the lower clip are those of
+// v_cvt_pk_u8_f32, which rounds half to even and saturates to [0, 255]
+// (checked on gfx950 over ties, their neighbours and out-of-range values):
+// after t = min(t, 127) it gives clip(rint(t), 0, 127) in one instruction
+// per output, packing included.  Without ReLU the 1.5 * 2^23 rounding and
+// med3 clip of EpiI8.
+template <bool SIDE, bool ORDER7, bool RELU>
+__device__ inline void halo_epilogue_tail(float (&t)[16], i32x4 side_chunk,
+                                          const float (&bias)[16], float sis, float lo_b,
+                                          float hi_b, uint32_t (&w)[4]) {
+  union {
+    int8_t b[16];
+    i32x4 v;
+  } sd;
+  sd.v = side_chunk;
+  if constexpr (SIDE) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = __builtin_fmaf(static_cast<float>(sd.b[e]), sis, t[e]);
+  }
+  if constexpr (!ORDER7) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = t[e] + bias[e];
+  }
+  if constexpr (RELU) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = __builtin_fminf(t[e], 127.0f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * j], 0u, 0u);
+      v = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * j + 1], 1u, v);
+      v = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * j + 2], 2u, v);
+      w[j] = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * j + 3], 3u, v);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      t[e] = __builtin_amdgcn_fmed3f(t[e] + kRoundMagic, lo_b, hi_b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = pack_word(pack_pair(__builtin_bit_cast(uint32_t, t[4 * j]),
+                                 __builtin_bit_cast(uint32_t, t[4 * j + 1])),
+                       pack_pair(__builtin_bit_cast(uint32_t, t[4 * j + 2]),
+                                 __builtin_bit_cast(uint32_t, t[4 * j + 3])));
+  }
+}
+
+template <int R, int S, bool SIDE, bool ORDER7, bool RELU>
 __global__ __launch_bounds__(kHaloThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_halo_i8_kernel(ConvArgs a) {
   constexpr int NKS = R * S;
@@ -1523,10 +1573,9 @@ void conv_halo_i8_kernel(ConvArgs a) {
   // Accumulator hand-off, per MFMA wave and step parity: chunk q (accumulator
   // tile q, 4 int32) of lane l at q * 1024 + 16 * l.
   __shared__ __attribute__((aligned(256))) char accb[4 * 2 * 4096];
-  // The slice's 64 bias values and per-channel scales (a copy's 64 lanes
-  // write 1 KiB: lanes past the 16 that carry values write zeros).
+  // The slice's 64 bias values (a copy's 64 lanes write 1 KiB: lanes past
+  // the 16 that carry values write zeros).
   __shared__ __attribute__((aligned(16))) float blds[256];
-  __shared__ __attribute__((aligned(16))) float clds[256];
 
   const int lane = threadIdx.x & 63;
   // readfirstlane: the wave index (and so the role) is uniform per wave.
@@ -1549,6 +1598,21 @@ void conv_halo_i8_kernel(ConvArgs a) {
   const HaloPhase PB = halo_phase(a, ga, g1, R);
   const int sA = (PA.ntile + 3) >> 2;  // steps of each phase (4 tiles per step)
   const int sB = (PB.ntile + 3) >> 2;
+
+  // The MFMA waves turn their accumulators into t = (float)acc * cis (or
+  // fmaf((float)acc, cis, bias) in the cuDNN 7 order) before the hand-off,
+  // so they need the scales (and, cuDNN 7, the bias) of their lane's 16
+  // channels: register loads issued here, which land with the copies the
+  // MFMA waves wait for before the first barrier.  K is a multiple of 16.
+  float cis_r[16], bias_r[16];
+  if (mfma_role) {
+    const bool live = ch0 < a.K;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {  // the [K] vectors are only 4-byte aligned
+      cis_r[e] = a.cis_vec && live ? a.cis_vec[ch0 + e] : a.cis;
+      bias_r[e] = ORDER7 && live ? a.bias[ch0 + e] : 0.0f;
+    }
+  }
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
@@ -1642,10 +1706,6 @@ void conv_halo_i8_kernel(ConvArgs a) {
         const uint32_t off = lane < 16 ? static_cast<uint32_t>((blockIdx.y * 64 + 4 * lane) * 4)
                                        : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)blds, 16, off, 0, 0, 0);
-        if (a.cis_vec)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              make_rsrc(a.cis_vec, static_cast<uint32_t>(a.K) * 4u), (lds_ptr_t)clds, 16, off, 0,
-              0, 0);
       } else {
         copy_rows(PB, xb, i - 1);
       }
@@ -1709,9 +1769,21 @@ void conv_halo_i8_kernel(ConvArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
+        // First steps of the requantisation, each an fp32 operation of the
+        // specification: t = (float)acc (nearest even), then * cis, or one
+        // fused multiply-add with the bias in the cuDNN 7 order.
         char* dst = accb + (m * 2 + ((step0 + ls) & 1)) * 4096 + 16 * lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<i32x4*>(dst + j * 1024) = acc[j];
+        for (int j = 0; j < 4; ++j) {
+          f32x4 t4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = static_cast<float>(acc[j][e]);
+            t4[e] = ORDER7 ? __builtin_fmaf(t, cis_r[4 * j + e], bias_r[4 * j + e])
+                           : t * cis_r[4 * j + e];
+          }
+          *reinterpret_cast<f32x4*>(dst + j * 1024) = t4;
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
         barrier();
       }
@@ -1739,9 +1811,6 @@ void conv_halo_i8_kernel(ConvArgs a) {
     float bias[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias[e] = blds[16 * g + e];
-    float cis[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) cis[e] = a.cis_vec ? clds[16 * g + e] : a.cis;
     const float sis = a.sis;
     const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
     auto epi_phase = [&](const HaloPhase& P, int steps, int step0) {
@@ -1779,7 +1848,18 @@ void conv_halo_i8_kernel(ConvArgs a) {
         }
         const bool ok = p < P.npx && ch0 < a.K;
         const uint32_t off = ok ? static_cast<uint32_t>((P.p0 * a.Wo + p) * a.K + ch0) : kOutOfRange;
-        stream_epilogue_i8<SIDE, 16, ORDER7>(acc, sd, bias, cis, sis, lo_b, hi_b, yr, off);
+        // The hand-off holds t as fp32 bits (bit-cast whole vectors: a
+        // bit-cast of one ext-vector element reads element 0).
+        float tv[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 f = __builtin_bit_cast(f32x4, acc[j]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tv[4 * j + e] = f[e];
+        }
+        uint32_t w[4];
+        halo_epilogue_tail<SIDE, ORDER7, RELU>(tv, sd, bias, sis, lo_b, hi_b, w);
+        store_words<16>(w, yr, off);
         if constexpr (SIDE) copy_side(t + 2);  // into the slot step t - 1 read
         if (t == 0 && sA >= 2) __builtin_amdgcn_s_waitcnt(SIDE ? 0x0f72 : 0x0f71);  // phase B's rows
         barrier();
@@ -2087,6 +2167,29 @@ bool halo_fits(const fconv_plan_s* p, int rows) {
   return true;
 }
 
+template <int R, int S, bool SIDE, bool ORDER7>
+void launch_halo_relu(dim3 g, const ConvArgs& a, hipStream_t s) {
+  if (a.relu)
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, SIDE, ORDER7, true>), g, dim3(kHaloThreads), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, SIDE, ORDER7, false>), g, dim3(kHaloThreads), 0,
+                       s, a);
+}
+
+template <int R, int S>
+hipError_t launch_halo_kernel(dim3 g, const ConvArgs& a, hipStream_t s) {
+  if (a.use_side && a.cudnn7)
+    launch_halo_relu<R, S, true, true>(g, a, s);
+  else if (a.use_side)
+    launch_halo_relu<R, S, true, false>(g, a, s);
+  else if (a.cudnn7)
+    launch_halo_relu<R, S, false, true>(g, a, s);
+  else
+    launch_halo_relu<R, S, false, false>(g, a, s);
+  return hipGetLastError();
+}
+
 template <int R, int S>
 hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStream_t s) {
   ConvArgs a = a0;
@@ -2099,15 +2202,7 @@ hipError_t launch_halo_shape(const fconv_plan_s* p, const ConvArgs& a0, hipStrea
   a.halo_rows = rows;
   a.halo_rows_a = std::min(kHaloRowsA, rows);
   const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows), static_cast<unsigned>(p->Kp / 64));
-  if (a.use_side && a.cudnn7)
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true, true>), g, dim3(kHaloThreads), 0, s, a);
-  else if (a.use_side)
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, true, false>), g, dim3(kHaloThreads), 0, s, a);
-  else if (a.cudnn7)
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false, true>), g, dim3(kHaloThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((conv_halo_i8_kernel<R, S, false, false>), g, dim3(kHaloThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_halo_kernel<R, S>(g, a, s);
 }
 
 hipError_t launch_halo(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) {

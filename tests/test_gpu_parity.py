@@ -195,17 +195,27 @@ def test_crafted_fma_and_contraction_cases():
         assert int(y[0, 0, 0, 0]) == exp
 
 
-def test_tie_dense_round_half_even():
-    """scale 0.5, bias 0, no side: every odd accumulator is an exact tie."""
+@pytest.mark.parametrize("relu", [False, True])
+@pytest.mark.parametrize("variant", [None, "stream", "rf", "general"])
+def test_tie_dense_round_half_even(relu, variant, monkeypatch):
+    """scale 0.5, bias 0, no side: every odd accumulator is an exact tie, on
+    both sides of zero (ReLU: ties at 0.5 and above round to even, below
+    clip to 0), in the default kernel for the shape (row-halo) and the
+    others."""
+    if variant:
+        monkeypatch.setenv("FCONV_FORCE_VARIANT", variant)
     rng = np.random.default_rng(21)
     x = wl.draw_int8(rng, (4, 12, 12, 64), -9, 9)
     w = wl.draw_int8(rng, (3, 3, 64, 64), -9, 9)
-    plan = make_plan(4, 12, 12, 64, 64, 3, 3, 1, "SAME", "int8", [wl.OP_SCALE, wl.OP_BIAS])
+    plan = make_plan(4, 12, 12, 64, 64, 3, 3, 1, "SAME", "int8",
+                     [wl.OP_SCALE, wl.OP_BIAS] + ([wl.OP_RELU] if relu else []))
+    assert plan.kernel_name.startswith("conv_" + (variant or "halo")), plan.kernel_name
     bias = np.zeros(64, np.float32)
     y, _ = run_gpu(plan, "int8", x, w, bias, None, 0.5)
     acc = oracle.conv_acc(x, w, 1, "SAME")
     assert np.mean(acc % 2 != 0) > 0.3
-    assert np.array_equal(y, np.clip(np.round(acc / 2.0), -128, 127).astype(np.int8))
+    lo = 0 if relu else -128
+    assert np.array_equal(y, np.clip(np.round(acc / 2.0), lo, 127).astype(np.int8))
 
 
 def test_zero_side_scale_skips_side():
