@@ -100,3 +100,39 @@ def test_gemm_is_deterministic():
     a, _ = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, None, bn=inp.bn)
     b, _ = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, None, bn=inp.bn)
     assert np.array_equal(a, b)
+
+
+def test_gemm_back_to_back_runs():
+    """Twelve runs with different inputs queued back to back on one stream,
+    no host wait between them, over a workspace filled with garbage before
+    the filter was packed (every fourth run repacks it): each run rewrites
+    every partial tile it sums, so every run's int8 output must equal the
+    oracle's bit for bit."""
+    rng = np.random.default_rng(4242)
+    N, H, C, K = 64, 4, 256, 512
+    dev = torch.device("cuda:0")
+    ops = [wl.OP_SCALE, wl.OP_SIDE, wl.OP_BIAS, wl.OP_RELU]
+    plan = make_plan(N, H, H, C, K, H, H, 1, "VALID", "int8", ops)
+    assert plan.kernel_name == "conv_gemm_i8"
+    w = wl.draw_int8(rng, (H, H, C, K), -128, 127)
+    bias = rng.normal(0, 20, K).astype(np.float32)
+    cis, sis = np.float32(1.0 / (H * H * C * 4)), np.float32(0.5)
+    ws = torch.full((plan.workspace_bytes,), 0x5A, dtype=torch.uint8, device=dev)
+    wd = torch.from_numpy(w).to(dev)
+    plan.pack_filter(wd, ws)
+    bd = torch.from_numpy(bias).to(dev)
+    runs = []
+    for i in range(12):
+        x = wl.draw_int8(rng, (N, H, H, C), -128, 127)
+        side = wl.draw_int8(rng, (N, 1, 1, K), -128, 127)
+        xd, sd = torch.from_numpy(x).to(dev), torch.from_numpy(side).to(dev)
+        y = torch.empty(plan.out_shape, dtype=torch.int8, device=dev)
+        plan.run(xd, wd, y, ws, bias=bd, side=sd, conv_input_scale=float(cis),
+                 side_input_scale=float(sis), prepacked=(i % 4 != 3))
+        runs.append((x, side, xd, sd, y))
+    torch.cuda.synchronize()
+    say("gemm back-to-back: 12 runs of %s queued, workspace %d B" % ((N, H, C, K), plan.workspace_bytes))
+    for i, (x, side, _, _, y) in enumerate(runs):
+        r = oracle.fused_conv_i8(x, w, bias, cis, side, sis, True, 1, "VALID")
+        got = y.cpu().numpy()
+        assert np.array_equal(got, r), "run %d: %d differ" % (i, np.count_nonzero(got != r))
