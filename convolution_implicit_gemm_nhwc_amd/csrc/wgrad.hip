@@ -61,6 +61,7 @@ struct fconv_wgrad_plan_s {
   bool dma;          // vec shapes: the direct-to-LDS kernel (else register-staged)
   int32_t ring;      // direct-to-LDS kernel: stages in its LDS ring (4 or 8)
   int32_t tk;        // output channels per tile (64, 128, or 256 with 8 waves)
+  bool ksplit;       // bf16 4-stage ring, 64/128-channel tile: two wave groups split each range
   int32_t tiles_k, tiles_kk;
   int32_t splits;    // pixel ranges
   int32_t m_per_split;
@@ -553,12 +554,18 @@ typedef __attribute__((address_space(3))) float* lds_f32_t;
 // [15:14]; expcnt and lgkmcnt at their maximum, i.e. not waited on).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int DT, int TK, int NBUF>
-__global__ __launch_bounds__(TK == 256 ? 512 : 256)  // DmaCfg::NW waves
+// KS = 2: two groups of NW waves, each with its own LDS ring, split the
+// workgroup's pixel range in two halves (group 0 the first, whole stages),
+// and group 1's tile is added to group 0's through LDS at the end.  A
+// workgroup then covers twice the pixels with the same waves per CU, so the
+// ranges, and the partial tiles written and summed, are halved.
+template <int DT, int TK, int NBUF, int KS>
+__global__ __launch_bounds__((TK == 256 ? 512 : 256) * KS)  // DmaCfg::NW waves per group
 __attribute__((amdgpu_waves_per_eu(NBUF == 8 ? 1 : 2, 2)))  // the 8-stage ring fills a CU's LDS
 void wgrad_dma_kernel(WgArgs a) {
   using Cfg = DmaCfg<DT, TK>;
   constexpr int ES = Cfg::ES, BM = Cfg::BM, NCW = Cfg::NCW, NW = Cfg::NW;
+  static_assert(KS == 1 || (KS == 2 && NW == 4 && NBUF == 4), "two groups of four waves, 4-stage rings");
   constexpr int E = 16 / ES;
   constexpr int WK = TK / 64;
   constexpr int WKK = NW / WK;
@@ -566,15 +573,15 @@ void wgrad_dma_kernel(WgArgs a) {
   constexpr int NJ = kWgTKK / WKK / 16;
   static_assert(NBUF == 4 || NBUF == 8, "ring of 4 or 8 stages");
   constexpr int SB_HI = NBUF > 4 ? Cfg::SB : 16;
-  __shared__ __attribute__((aligned(1024))) char buf0[Cfg::SB];
-  __shared__ __attribute__((aligned(1024))) char buf1[Cfg::SB];
-  __shared__ __attribute__((aligned(1024))) char buf2[Cfg::SB];
-  __shared__ __attribute__((aligned(1024))) char buf3[Cfg::SB];
+  // Stage buffer i of group q at bufi + q * SB.
+  __shared__ __attribute__((aligned(1024))) char buf0[KS * Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf1[KS * Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf2[KS * Cfg::SB];
+  __shared__ __attribute__((aligned(1024))) char buf3[KS * Cfg::SB];
   __shared__ __attribute__((aligned(1024))) char buf4[SB_HI];
   __shared__ __attribute__((aligned(1024))) char buf5[SB_HI];
   __shared__ __attribute__((aligned(1024))) char buf6[SB_HI];
   __shared__ __attribute__((aligned(1024))) char buf7[SB_HI];
-  char* const bufs[8] = {buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7};
 
   const int nb = gridDim.x;
   const int b = blockIdx.x;
@@ -585,14 +592,23 @@ void wgrad_dma_kernel(WgArgs a) {
   const int tile = logical % tiles;
   const int k0 = (tile % a.tiles_k) * TK;
   const int kk0 = (tile / a.tiles_k) * kWgTKK;
-  const int m_begin = split * a.m_per_split;
-  const int m_end = min(a.M, m_begin + a.m_per_split);
-  const int nst = (m_end - m_begin + BM - 1) / BM;
+  const int r_begin = split * a.m_per_split;
+  const int r_end = min(a.M, r_begin + a.m_per_split);
+  const int r_st = (r_end - r_begin + BM - 1) / BM;  // stages of the range
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave0 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave0 / NW;      // wave group (KS = 2), else 0
+  const int wave = wave0 % NW;     // wave inside the group
   const int wk = wave % WK, wkk = wave / WK;
+  // The group's pixels [m_begin, m_end) and the stages every group steps
+  // through (group 1's past its pixels copy zeros).
+  const int nst = (r_st + KS - 1) / KS;
+  const int m_begin = r_begin + grp * nst * BM;
+  const int m_end = min(r_end, m_begin + nst * BM);
+  char* const bufs[8] = {buf0 + grp * Cfg::SB, buf1 + grp * Cfg::SB, buf2 + grp * Cfg::SB,
+                         buf3 + grp * Cfg::SB, buf4, buf5, buf6, buf7};
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
@@ -783,6 +799,35 @@ void wgrad_dma_kernel(WgArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
 
+  if constexpr (KS == 2) {
+    // Group 1 hands its tile to group 0 through the stage buffers (every
+    // wave has read its last stage before the barrier): piece t = i*NJ + j
+    // of wave w at buffer t % 4, offset (w * NI*NJ/4 + t/4) KiB.
+    static_assert(NW * (NI * NJ / 4) * 1024 <= KS * Cfg::SB, "hand-off fits the stage buffers");
+    char* const hb[4] = {buf0, buf1, buf2, buf3};
+    barrier();
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int t = i * NJ + j;
+          *reinterpret_cast<f32x4*>(hb[t % 4] + (wave * (NI * NJ / 4) + t / 4) * 1024 + 16 * lane) =
+              acc[i][j];
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the hand-off is written
+    barrier();
+    if (grp == 1) return;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t = i * NJ + j;
+        acc[i][j] += *reinterpret_cast<const f32x4*>(
+            hb[t % 4] + (wave * (NI * NJ / 4) + t / 4) * 1024 + 16 * lane);
+      }
+  }
   wg_store<NI, NJ>(a, acc, split, k0, kk0, wk, wkk, lane);
 }
 
@@ -840,17 +885,21 @@ hipError_t launch_wgrad_main(const WgArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int TK, int NBUF>
+template <int DT, int TK, int NBUF, int KS = 1>
 hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
   const int grid = (a.blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF>), dim3(grid), dim3(DmaCfg<DT, TK>::NW * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((wgrad_dma_kernel<DT, TK, NBUF, KS>), dim3(grid),
+                     dim3(DmaCfg<DT, TK>::NW * KS * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
   if (p->dma && p->tk == 256) return launch_wgrad_dma<DT, 256, 4>(a, s);
+  if constexpr (DT == FCONV_BF16) {
+    if (p->dma && p->ksplit)
+      return p->tk == 128 ? launch_wgrad_dma<DT, 128, 4, 2>(a, s) : launch_wgrad_dma<DT, 64, 4, 2>(a, s);
+  }
   if (p->dma)
     return p->ring == 8
                ? (p->tk == 128 ? launch_wgrad_dma<DT, 128, 8>(a, s) : launch_wgrad_dma<DT, 64, 8>(a, s))
@@ -868,8 +917,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
-const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring) {
+const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring, bool ksplit) {
   if (dma && tk == 256) return "wgrad_dma_bf16_256";
+  if (dma && ksplit) return tk == 128 ? "wgrad_dma2_bf16_128" : "wgrad_dma2_bf16_64";
   if (dma && ring == 8) {
     if (dtype == FCONV_BF16) return tk == 128 ? "wgrad_dma8_bf16_128" : "wgrad_dma8_bf16_64";
     return tk == 128 ? "wgrad_dma8_f32_128" : "wgrad_dma8_f32_64";
@@ -941,22 +991,32 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   const char* ring = getenv("FCONV_WGRAD_RING");
   p->ring = d.dtype == FCONV_FP32 ? 8 : 4;
   if (ring && (atoi(ring) == 4 || atoi(ring) == 8)) p->ring = atoi(ring);
-  // Tile width: 256 output channels (eight waves, one workgroup per CU,
-  // a quarter fewer operand bytes per flop) for bf16 with K > 128 on the
-  // 4-stage ring; else 128, or 64 for K <= 64.
+  // Tile width: 128 output channels, or 64 for K <= 64.  FCONV_WGRAD_TK=256
+  // pins 256-channel tiles (eight waves of 64x64, one workgroup per CU, a
+  // quarter fewer operand bytes per flop) for bf16 with K > 128 on the
+  // 4-stage ring: as fast as two wave groups on 128-channel tiles on the
+  // 28x28x256 layer, with twice their pixel ranges and partial sums.
   const char* tk_env = getenv("FCONV_WGRAD_TK");
-  const bool wide = p->dma && d.dtype == FCONV_BF16 && p->ring == 4 && d.K > 128 &&
-                    !(tk_env && atoi(tk_env) == 128);
+  const bool wide = p->dma && d.dtype == FCONV_BF16 && p->ring == 4 && d.K > 128 && tk_env &&
+                    atoi(tk_env) == 256;
   p->tk = wide ? 256 : d.K > 64 ? 128 : 64;
+  // Two wave groups per workgroup splitting each pixel range (bf16, 4-stage
+  // ring, 64/128-channel tiles): one workgroup of eight waves per CU instead
+  // of two of four, half the ranges.  FCONV_WGRAD_GROUPS=1 pins one group.
+  const char* groups = getenv("FCONV_WGRAD_GROUPS");
+  p->ksplit = p->dma && d.dtype == FCONV_BF16 && p->ring == 4 && p->tk != 256 &&
+              !(groups && atoi(groups) == 1);
   p->tiles_k = (d.K + p->tk - 1) / p->tk;
   p->tiles_kk = (p->Kg + kWgTKK - 1) / kWgTKK;
   const int64_t tiles = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
-  // Pixel ranges, each at least four stages long: one workgroup per CU with
-  // the 8-stage ring or the 256-channel tile, else about two per CU.
-  const bool one_per_cu = p->dma && (p->ring == 8 || p->tk == 256);
+  // Pixel ranges, each at least four stages long per wave group: one
+  // workgroup per CU with the 8-stage ring, the 256-channel tile or two wave
+  // groups, else about two per CU.
+  const bool one_per_cu = p->dma && (p->ring == 8 || p->tk == 256 || p->ksplit);
   int64_t splits = one_per_cu ? kWgTargetBlocks / 2 / tiles
                               : (kWgTargetBlocks + tiles - 1) / tiles;
-  const int64_t max_splits = (p->M + 4 * bm - 1) / (4 * bm);
+  const int64_t min_stages = p->ksplit ? 8 : 4;
+  const int64_t max_splits = (p->M + min_stages * bm - 1) / (min_stages * bm);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int64_t mps = (p->M + splits - 1) / splits;
@@ -974,7 +1034,7 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->ws_bytes = splits > 1 ? static_cast<size_t>(splits * p->lp * 4) : 0;
   p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
-  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring);
+  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring, p->ksplit);
   // FCONV_LOG=1 (environment): the plan's decisions on stderr.
   const char* lg = getenv("FCONV_LOG");
   if (lg && *lg && strcmp(lg, "0") != 0)

@@ -63,19 +63,22 @@ def _pin(kernel, monkeypatch):
         monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
     elif kernel in ("ring4", "ring8"):
         monkeypatch.setenv("FCONV_WGRAD_RING", kernel[-1])
-    elif kernel == "tk128":
-        monkeypatch.setenv("FCONV_WGRAD_TK", "128")
+    elif kernel == "tk256":
+        monkeypatch.setenv("FCONV_WGRAD_TK", "256")
+    elif kernel == "groups1":
+        monkeypatch.setenv("FCONV_WGRAD_GROUPS", "1")
 
 
-@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk128", "staged"])
+@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk256", "groups1", "staged"])
 @pytest.mark.parametrize("out_fp32", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", CASES)
 def test_wgrad_small_shapes(case, dtype, out_fp32, kernel, monkeypatch):
     """Every kernel: the direct-to-LDS one (where C and K fill 16-byte chunks)
     with its 4- and 8-stage rings (FCONV_WGRAD_RING; the default is 4 for
-    bf16, 8 for fp32), bf16 with K > 128 on 128- instead of 256-channel tiles
-    (FCONV_WGRAD_TK=128), and the register-staged one
+    bf16, 8 for fp32), bf16 with K > 128 on 256- instead of 128-channel tiles
+    (FCONV_WGRAD_TK=256), bf16 64/128-channel tiles with one wave group
+    instead of two (FCONV_WGRAD_GROUPS=1), and the register-staged one
     (FCONV_WGRAD_KERNEL=staged)."""
     if dtype == "fp32" and out_fp32:
         pytest.skip("fp32 plans always write fp32")
@@ -126,7 +129,7 @@ def test_wgrad_is_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk128", "staged"])
+@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk256", "groups1", "staged"])
 @pytest.mark.parametrize("name", list(wl.WGRAD_LAYERS))
 def test_wgrad_full_workload(name, kernel, monkeypatch):
     """The full benchmark workloads, every element against the oracle."""

@@ -80,7 +80,8 @@ def test_workloads_and_workspace():
         kg_k = L.R * L.S * L.C * L.K
         # partial sums: a whole number of fp32 dW copies (or none)
         assert g.workspace_bytes % (4 * ((kg_k + 3) // 4)) == 0
-        assert g.kernel_name.startswith("wgrad_dma_bf16" if L.dtype == "bf16" else "wgrad_dma8_f32")
+        assert g.kernel_name.startswith(("wgrad_dma_bf16", "wgrad_dma2_bf16") if L.dtype == "bf16"
+                                        else "wgrad_dma8_f32")
 
 
 def test_run_checks_arguments():
@@ -129,12 +130,20 @@ def test_staged_kernel_can_be_pinned(monkeypatch):
     g = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g.kernel_name == "wgrad_bf16_128"
     monkeypatch.delenv("FCONV_WGRAD_KERNEL")
-    assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16").kernel_name == \
-        "wgrad_dma_bf16_256"
-    monkeypatch.setenv("FCONV_WGRAD_TK", "128")
+    g2 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
+    assert g2.kernel_name == "wgrad_dma2_bf16_128"
+    monkeypatch.setenv("FCONV_WGRAD_TK", "256")
+    g256 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
+    assert g256.kernel_name == "wgrad_dma_bf16_256"
+    # two wave groups on 128-channel tiles: half the ranges of 256-channel tiles
+    assert g256.workspace_bytes == 2 * g2.workspace_bytes
+    monkeypatch.delenv("FCONV_WGRAD_TK")
+    monkeypatch.setenv("FCONV_WGRAD_GROUPS", "1")
     g4 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g4.kernel_name == "wgrad_dma_bf16_128"
-    monkeypatch.delenv("FCONV_WGRAD_TK")
+    # two wave groups per workgroup: half the pixel ranges of one group
+    assert g4.workspace_bytes == 2 * g2.workspace_bytes
+    monkeypatch.delenv("FCONV_WGRAD_GROUPS")
     assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "fp32").kernel_name == \
         "wgrad_dma8_f32_128"
     monkeypatch.setenv("FCONV_WGRAD_RING", "8")
