@@ -1049,6 +1049,266 @@ void conv_tile_kernel(ConvArgs a) {
   }
 }
 
+// Tall variant of the tiled kernel, for grids whose 128-pixel tiles would
+// need a second round over the CUs while 256-pixel ones fit in one (the
+// strided 56x56x128 layer: 392 tiles against 196).  Tile 256 pixels x 128
+// channels, the same 8 waves as a 4 x 2 grid of 64 pixels x 64 channels
+// (each lane ends with 16 consecutive channels of 4 pixels), the same
+// 128-byte stages, slot swizzle and buffer->LDS copies (6 per wave per stage:
+// 4 of pixel rows, 2 of filter rows), but three 48 KiB stage buffers with the
+// copies two stages ahead: a stage's MFMAs take twice as long as in the
+// 128-pixel tile, so one step covers the copies' latency, and a quarter fewer
+// bytes are copied per MFMA.  Epilogue values (bias, scales, the float
+// vectors) are copied to LDS before stage 0; the int8 side input is loaded
+// from global memory at the end (LDS has no room for it).
+constexpr int kTall = 256;
+constexpr int kTallStage = (kTall + kTileBN) * kTileStage;  // 48 KiB
+
+template <int DT, bool KVEC>
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void conv_tile256_kernel(ConvArgs a) {
+  using Acc = typename Dt<DT>::Acc;
+  constexpr int E = Dt<DT>::kChunk;
+  constexpr int ES = 16 / E;
+  constexpr int SE = kTileStage / ES;       // reduction elements per stage
+  constexpr int CPS = 6;                    // copies per wave per stage
+  constexpr int MI = DT == FCONV_FP32 ? 4 : 1;  // MFMA instructions per chunk product
+  constexpr int MPS = 32 * MI;              // MFMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) char buf0[kTallStage];
+  __shared__ __attribute__((aligned(1024))) char buf1[kTallStage];
+  __shared__ __attribute__((aligned(1024))) char buf2[kTallStage];
+  // int8: bias and per-channel scales of the tile's 128 channels (1 KiB slot
+  // each, 512 bytes used); float: bias, gamma, var, mean, beta.
+  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 2048 : 5 * 1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;  // 64-pixel quarter, 64-channel half
+  const int g = lane >> 4, col = lane & 15;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+
+  // Copy roles: pixel copy h (0..3) of this wave fills tile rows
+  // 64h + 8*wave .. +7, filter copy h (0..1) filter rows 64h + 8*wave .. +7
+  // (tile rows 256 + the same); lane l fills slot l & 7 of row r0 + 64h,
+  // i.e. chunk q = (l & 7) ^ ((l >> 3) & 7) of that row.
+  const int r0 = 8 * wave + (lane >> 3);
+  const int q = (lane & 7) ^ ((lane >> 3) & 7);
+  int hb[4], wb[4], pbase[4];
+  uint32_t wbase[2];
+  const int RS = a.wrow_bytes;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int m = blockIdx.x * kTall + r0 + 64 * h;
+    const int mm = m < a.M ? m : 0;
+    const uint32_t qq = fast_div(static_cast<uint32_t>(mm), a.wo_mul, a.wo_add, a.wo_shift);
+    const int wo = mm - static_cast<int>(qq) * a.Wo;
+    const uint32_t n = fast_div(qq, a.ho_mul, a.ho_add, a.ho_shift);
+    const int ho = static_cast<int>(qq) - static_cast<int>(n) * a.Ho;
+    hb[h] = m < a.M ? ho * a.sh - a.pt : -(1 << 20);
+    wb[h] = wo * a.sw - a.pl;
+    pbase[h] = static_cast<int>(n) * a.H * a.W * a.C * ES + q * 16;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + r0 + 64 * h) * RS + q * 16);
+
+  // Packed row blockIdx.y*128 + wn*64 + 16j + 4g + v is channel
+  // 128*blockIdx.y + 64*wn + 16g + 4j + v: 16 consecutive channels per lane.
+  const int ch0 = blockIdx.y * kTileBN + wn * 64 + 16 * g;
+  {
+    // Epilogue vectors, before the first stage's copies (the wait for stage
+    // 0 covers them); zeros past K and for an absent op.
+    const int nv = DT == FCONV_INT8 ? 2 : 5;
+    if (wave < nv) {
+      const float* src;
+      bool use;
+      if constexpr (DT == FCONV_INT8) {
+        src = wave == 0 ? a.bias : a.cis_vec;
+        use = src != nullptr;
+      } else {
+        src = wave == 0 ? a.bias : wave == 1 ? a.bn_gamma : wave == 2 ? a.bn_var
+            : wave == 3 ? a.bn_mean : a.bn_beta;
+        use = wave == 0 ? a.use_bias != 0 : a.use_bn != 0;
+      }
+      const __amdgpu_buffer_rsrc_t pr =
+          make_rsrc(use ? src : nullptr, use ? static_cast<uint32_t>(a.K) * 4u : 0u);
+      const uint32_t off =
+          lane < 32 ? static_cast<uint32_t>((blockIdx.y * kTileBN + 4 * lane) * 4) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)(epar + wave * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  const int nst = a.R * a.S * (a.C / SE);
+  const int CB = a.C * ES;  // bytes of one tap's channels
+  int nx_st = 0, nx_c0b = 0, nx_r = 0, nx_s = 0;
+  auto issue = [&](char* buf) __attribute__((always_inline)) {
+    const int st = nx_st, c0b = nx_c0b, r = nx_r, s = nx_s;
+    ++nx_st;
+    nx_c0b += kTileStage;
+    if (nx_c0b == CB) {
+      nx_c0b = 0;
+      if (++nx_s == a.S) {
+        nx_s = 0;
+        ++nx_r;
+      }
+    }
+    const bool live = st < nst;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int hi = hb[h] + r, wi = wb[h] + s;
+      const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                      static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+      const uint32_t off =
+          ok ? static_cast<uint32_t>(pbase[h] + (hi * a.W + wi) * a.C * ES + c0b) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_ptr_t)(buf + (8 * wave + 64 * h) * kTileStage), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_ptr_t)(buf + (kTall + 8 * wave + 64 * h) * kTileStage), 16,
+          live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0, 0);
+  };
+
+  Acc acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  // Fragment rows: pixel row wm*64 + 16i + col, filter row 256 + wn*64 +
+  // 16j + col; both have (row & 7) == (col & 7).
+  struct Frags {
+    i32x4 pf[2][4], ff[2][4];
+  };
+  auto read_frags = [&](const char* buf, Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t slot = static_cast<uint32_t>(((kk * 4 + g) ^ (col & 7)) * 16);
+      const char* pl = buf + (wm * 64 + col) * kTileStage + slot;
+      const char* fb = buf + (kTall + wn * 64 + col) * kTileStage + slot;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
+    }
+  };
+  auto mma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mma_chunk(f.ff[kk][j], f.pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Step st: wait for this wave's copies of stage st + 1 (issued one step
+  // earlier; nothing later is in flight), a plain barrier (LDS has no cache:
+  // every wave's copies of stage st + 1 are visible after it, and every wave
+  // has read stage st - 1's fragments), copy stage st + 2 into stage
+  // st - 1's buffer, read stage st + 1's fragments while stage st's MFMAs
+  // run.
+  auto step = [&](const char* next, char* next2, const Frags& cur, Frags& nxt)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    barrier();
+    issue(next2);
+    read_frags(next, nxt);
+    mma(cur);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // DS read
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MPS / CPS, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the copy)
+    }
+    if constexpr (MPS % CPS != 0) __builtin_amdgcn_sched_group_barrier(0x008, MPS % CPS, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Stage st lives in buffer st % 3: whole trips of three stages, then the
+  // rest.  Past the last stage the copies are zeros and the fragment reads
+  // unused.
+  issue(buf0);
+  issue(buf1);
+  Frags fa, fb;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS));  // this wave's copies of stage 0 (and the vectors)
+  barrier();
+  read_frags(buf0, fa);
+  int st = 0;
+  for (; st + 6 <= nst; st += 6) {
+    step(buf1, buf2, fa, fb);
+    step(buf2, buf0, fb, fa);
+    step(buf0, buf1, fa, fb);
+    step(buf1, buf2, fb, fa);
+    step(buf2, buf0, fa, fb);
+    step(buf0, buf1, fb, fa);
+  }
+  // The rest (0..5 stages), starting from buffer 0 with fa current.
+  if (st < nst) step(buf1, buf2, fa, fb);
+  if (st + 1 < nst) step(buf2, buf0, fb, fa);
+  if (st + 2 < nst) step(buf0, buf1, fa, fb);
+  if (st + 3 < nst) step(buf1, buf2, fb, fa);
+  if (st + 4 < nst) step(buf2, buf0, fa, fb);
+  __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
+
+  if (ch0 >= a.K) return;
+  const int cl = ch0 - blockIdx.y * kTileBN;
+  const float* ep = reinterpret_cast<const float*>(epar) + cl;
+  if constexpr (DT == FCONV_INT8) {
+    float bias_l[16], cis_l[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      bias_l[e] = ep[e];
+      cis_l[e] = a.cis_vec ? ep[256 + e] : a.cis;
+    }
+    i32x4 sd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTall + wm * 64 + i * 16 + col;
+      sd[i] = a.use_side && m < a.M ? load_side_chunk<16>(a, m, ch0, KVEC) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTall + wm * 64 + i * 16 + col;
+      if (m >= a.M) continue;
+      int32_t v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      epilogue_store_i8<16>(v, a, m, ch0, KVEC, sd[i], bias_l, cis_l);
+    }
+  } else {
+    FloatEpiParams<16> fpar;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      fpar.bias[e] = a.use_bias ? ep[e] : 0.0f;
+      fpar.sc[e] = a.use_bn ? ep[256 + e] / __builtin_sqrtf(ep[512 + e] + a.bn_eps) : 0.0f;
+      fpar.mean[e] = a.use_bn ? ep[768 + e] : 0.0f;
+      fpar.beta[e] = a.use_bn ? ep[1024 + e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = blockIdx.x * kTall + wm * 64 + i * 16 + col;
+      if (m >= a.M) continue;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      epilogue_store_float<DT, 16>(v, a, m, ch0, KVEC, fpar);
+    }
+  }
+}
+
 // ------------------------------------------------------- streaming conv
 
 // int8 requantisation, cuDNN 8 order (TensorFlow conv_ops_fused_int8.cc,
@@ -2228,9 +2488,17 @@ hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   // on the 256-channel bf16 layer).
   // 64-pixel tiles where 128-pixel ones would leave at least half the CUs
   // idle (the CBNA layers: 98 tiles), unless the plan pins the height.
+  // 256-pixel tiles where 128-pixel ones would need a second round over the
+  // CUs and 256-pixel ones fit in one (the strided int8 layer: 392 -> 196).
   const int64_t tiles = static_cast<int64_t>(grid.x) * grid.y;
-  const bool bm64 = p->pixel_tiles == 1 || (p->pixel_tiles == 0 && tiles * 2 <= device_cu_count());
-  if (bm64) {
+  const int64_t cus = device_cu_count();
+  const int64_t tall_tiles = (p->M + kTall - 1) / kTall * grid.y;
+  const bool tall = p->pixel_tiles == 4 || (p->pixel_tiles == 0 && tiles > cus && tall_tiles <= cus);
+  const bool bm64 = p->pixel_tiles == 1 || (p->pixel_tiles == 0 && tiles * 2 <= cus);
+  if (tall) {
+    const dim3 grid256(static_cast<unsigned>((p->M + kTall - 1) / kTall), grid.y);
+    hipLaunchKernelGGL((conv_tile256_kernel<DT, true>), grid256, dim3(kTileThreads), 0, s, a);
+  } else if (bm64) {
     const dim3 grid64(static_cast<unsigned>((p->M + 63) / 64), grid.y);
     if (p->d.K <= kTileBN)
       hipLaunchKernelGGL((conv_tile_kernel<DT, true, true, 64>), grid64, dim3(kTileThreads), 0, s, a);

@@ -94,8 +94,9 @@ constexpr int64_t kRfMaxLds = 80 * 1024;
 // comparisons (a full-size VALID filter takes the GEMM kernel unless another
 // family is pinned);
 // FCONV_RF_PT=1|2|4 overrides the pixel tiles, FCONV_HALO_ROWS the output rows
-// per workgroup of the row-halo kernel, FCONV_TILE_BM=64|128 the pixel rows
-// of the tiled kernel's tile (otherwise chosen at launch from the grid size).
+// per workgroup of the row-halo kernel, FCONV_TILE_BM=64|128|256 the pixel
+// rows of the tiled kernel's tile (otherwise chosen at launch from the grid
+// size).
 void choose_variant(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
   p->variant = kGeneral;
@@ -127,6 +128,7 @@ void choose_variant(fconv_plan_s* p) {
     const char* bm = getenv("FCONV_TILE_BM");
     if (bm && atoi(bm) == 64) p->pixel_tiles = 1;
     if (bm && atoi(bm) == 128) p->pixel_tiles = 2;
+    if (bm && atoi(bm) == 256) p->pixel_tiles = 4;
   } else if (!force_general && p->load_mode == kLoadTap && d.K % 16 == 0 && rf_lds <= kRfMaxLds &&
       sizes_ok) {
     p->variant = kResidentFilter;
@@ -279,6 +281,7 @@ int list_configs(const fconv_plan_s* p, KernelConfig* out, int max) {
     add(kTiled, 0, 0, 0);
     add(kTiled, 1, 0, 0);
     add(kTiled, 2, 0, 0);
+    add(kTiled, 4, 0, 0);
   }
   if (f.rf) {
     static const int32_t pt_rd[6][2] = {{1, 4}, {1, 9}, {2, 4}, {2, 9}, {4, 2}, {4, 4}};

@@ -58,7 +58,7 @@ struct fconv_plan_s {
   int32_t load_mode;
   int32_t variant;
   int32_t pixel_tiles;  // kResidentFilter: 16-pixel MFMA tiles per wave (1, 2, 4);
-                        // kTiled: 64-pixel rows of the tile (1, 2; 0 = by grid size)
+                        // kTiled: 64-pixel rows of the tile (1, 2, 4; 0 = by grid size)
   int32_t ring_depth;   // kResidentFilter: k-steps of patch loads in flight
   int32_t halo_rows;    // kHalo: output rows per workgroup, 0 = sized to the device
   int32_t wrow_bytes;   // packed filter row stride: KgP * esize + 16 (zero pad)

@@ -385,16 +385,17 @@ def test_full_size_valid(C, K, R, variant, dtype, monkeypatch):
 
 
 
-@pytest.mark.parametrize("bm", [64, 128])
+@pytest.mark.parametrize("bm", [64, 128, 256])
 @pytest.mark.parametrize("K", [64, 256])
 @pytest.mark.parametrize("dtype,C,R,stages", [
     ("int8", 128, 1, 1), ("int8", 256, 1, 2), ("fp32", 96, 1, 3), ("int8", 128, 2, 4),
-    ("fp32", 160, 1, 5), ("fp32", 224, 1, 7), ("bf16", 64, 3, 9)])
+    ("fp32", 160, 1, 5), ("bf16", 384, 1, 6), ("fp32", 224, 1, 7), ("bf16", 64, 3, 9),
+    ("fp32", 384, 1, 12)])
 def test_tile_stage_counts(dtype, C, R, stages, K, bm, monkeypatch):
-    """The tiled kernel's loop tails: every stage count from 1 to 9 modulo
-    the 4-buffer ring, with one 128-channel tile (K = 64: two stages per
-    barrier) and with two (K = 256: one stage per barrier), in both tile
-    heights."""
+    """The tiled kernel's loop tails: every stage count from 1 to 9 and 12,
+    modulo the 4-buffer ring of the 64- and 128-pixel tiles (one 128-channel
+    tile, K = 64: two stages per barrier; two, K = 256: one per barrier) and
+    modulo the 6-stage loop trip of the 256-pixel tile's 3-buffer ring."""
     esize = {"int8": 1, "bf16": 2, "fp32": 4}[dtype]
     assert R * R * C * esize // 128 == stages
     monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
@@ -407,11 +408,12 @@ def test_tile_stage_counts(dtype, C, R, stages, K, bm, monkeypatch):
     (128, 64, 9, 13, 3, 1, "SAME"), (128, 128, 11, 11, 3, 2, "SAME"),
     (256, 64, 7, 9, 1, 1, "VALID"), (256, 256, 5, 5, 3, 1, "SAME"), (128, 192, 8, 8, 8, 1, "VALID")])
 @pytest.mark.parametrize("dtype", ["int8", "bf16", "fp32"])
-def test_tile_shapes_128_pixel_tiles(C, K, H, W, R, stride, pad, dtype, monkeypatch):
-    """Ragged shapes with 128-pixel tiles pinned (small grids pick 64-pixel
-    tiles by themselves)."""
+@pytest.mark.parametrize("bm", [128, 256])
+def test_tile_shapes_pinned_heights(C, K, H, W, R, stride, pad, dtype, bm, monkeypatch):
+    """Ragged shapes with 128- and 256-pixel tiles pinned (small grids pick
+    64-pixel tiles by themselves)."""
     monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
-    monkeypatch.setenv("FCONV_TILE_BM", "128")
+    monkeypatch.setenv("FCONV_TILE_BM", str(bm))
     tol = TOL["fp32"] if R * R * C > 4096 else 2e-6
     name = check_case(tile_case(C, K, H, W, R, stride, pad, dtype), dtype, fp32_tol=tol)
     assert name.startswith("conv_tile_"), name
