@@ -49,6 +49,12 @@ def _code_only(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
+LAUNCH_NOTE = ("hip graph of the K steps, replayed once (value, ms_per_step: host wall clock "
+               "with a synchronize on both sides; graph_event_us_per_step: HIP events around "
+               "that replay); roofline.kernel_avg_us: HIP events around a second replay of "
+               "the same graph queued behind a spin kernel, i.e. the launches' own GPU time")
+
+
 def kernel_source_hash(sources=None) -> str:
     """Hash of the code of the kernel sources the counters were taken on (the
     forward kernels' by default; an entry may name its own files)."""
@@ -169,6 +175,25 @@ def copy_probe(nbytes: int, steps: int, warmup: int):
           flush=True)
 
 
+def gated_graph_ms(graph, gstream, steps: int) -> float:
+    """GPU time per launch of one replay of `graph` (`steps` launches).  The
+    stream is first held by a short spin kernel (~1 ms), so the host has
+    queued the whole graph before the first event is stamped: the events
+    bracket the launches themselves, not the host-side launch of the graph,
+    which a replay timed on its own also includes (~1.3 us per step at 20
+    steps)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gstream):
+        torch.cuda._sleep(2_000_000)
+        e0.record(gstream)
+        graph.replay()
+        e1.record(gstream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def wgrad_cpu_baseline(L, inp, seconds: float):
     """The oracle's weight gradient on a prefix of the batch (one image, then
     more while the budget lasts), as FLOP/s of the same formula."""
@@ -253,7 +278,8 @@ def bench_wgrad(args):
     g1.record(gstream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = g0.elapsed_time(g1) / args.steps
+    graph_event_ms = g0.elapsed_time(g1) / args.steps
+    step_ms = gated_graph_ms(graph, gstream, args.steps)
 
     ops = L.ops_count()
     esize = 2 if L.dtype == "bf16" else 4
@@ -281,8 +307,9 @@ def bench_wgrad(args):
                    "padding": L.padding, "kernel": kernels,
                    "pixel_ranges": plan.workspace_bytes // (16 * ((L.R * L.S * L.C * L.K + 3)
                                                                  // 4)) or 1},
-        "launch": "hip graph of the K steps, replayed once",
+        "launch": LAUNCH_NOTE,
         "pct_of_mfma_peak": round(100.0 * value / peak, 3),
+        "graph_event_us_per_step": round(graph_event_ms * 1e3, 3),
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
                   "event_us_per_step": round(eager_ms * 1e3, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -460,7 +487,8 @@ def main():
     g1.record(gstream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = g0.elapsed_time(g1) / args.steps
+    graph_event_ms = g0.elapsed_time(g1) / args.steps
+    kernel_ms = gated_graph_ms(graph, gstream, args.steps)
     y_gpu = y.cpu()
 
     # Cold: last-level cache flushed before each singly timed step.
@@ -525,8 +553,9 @@ def main():
                      (order, "per-channel" if args.per_channel_scale else "scalar")
                      if L.dtype == "int8" else "bias, batch norm, " +
                      (args.activation or "relu")),
-        "launch": "hip graph of the K steps, replayed once",
+        "launch": LAUNCH_NOTE,
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TOPS[L.dtype], 3),
+        "graph_event_us_per_step": round(graph_event_ms * 1e3, 3),
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
                   "ms_per_step": round(wall_eager / args.steps * 1e3, 6),
                   "event_us_per_step": round(eager_ms * 1e3, 3)},
