@@ -174,6 +174,23 @@ __global__ __launch_bounds__(256) void pack_filter_kernel(const void* __restrict
 
 // ---------------------------------------------------------------- epilogues
 
+// Cache policy of output stores.  y is written once and never read back by
+// the kernel.  Non-temporal (nt) instead of the default measured 0.3 us
+// faster on the 3x3 int8 layer and 0.55 us on the 1x1.  Where a wave writes
+// whole lines (int8 with 16 channels per lane: four lanes write 64
+// contiguous bytes, a wave 16 pixels x 64 channels of contiguous NHWC), sc1
+// (device-scope write-through) on top of nt measured faster again: 3x3 int8
+// 8.26 -> 8.00 us, 1x1 6.67 -> 6.23, strided int8 (256-pixel tiles) 20.0 ->
+// 18.6.  bf16 and fp32 tiles, whose waves write partial lines, were 3-8%
+// slower with sc1 and keep nt (bf16) or the default (fp32).
+constexpr int kStoreNT = 2;
+constexpr int kStoreLines = 16 | kStoreNT;
+
+__device__ inline __amdgpu_buffer_rsrc_t output_rsrc(const void* y, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(y), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
@@ -258,7 +275,10 @@ __device__ inline void epilogue_store_i8(const int32_t (&v)[NCH], const ConvArgs
   }
   if (kvec) {
     if constexpr (NCH == 16)
-      __builtin_nontemporal_store(o.v, reinterpret_cast<i32x4*>(y));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          o.v, output_rsrc(a.y, a.y_bytes),
+          static_cast<uint32_t>(m) * static_cast<uint32_t>(a.K) + static_cast<uint32_t>(ch0), 0,
+          kStoreLines);
     else
       __builtin_nontemporal_store(i32x2{o.v.x, o.v.y}, reinterpret_cast<i32x2*>(y));
   } else {
@@ -1343,11 +1363,6 @@ __device__ inline uint32_t pack_word(uint32_t lo_pair, uint32_t hi_pair) {
   return __builtin_amdgcn_perm(hi_pair, lo_pair, 0x05040100u);  // [lo.b0, lo.b1, hi.b0, hi.b1]
 }
 
-// Cache policy of int8 and bf16 output stores: non-temporal.  y is written
-// once and never read back by the kernel; streaming it out instead of leaving
-// it resident in L2 measured 0.3 us faster on the 3x3 int8 layer and 0.55 us
-// on the 1x1 (the fp32 stores of the tiled kernel were 1% slower with it).
-constexpr int kStoreNT = 2;
 
 // One lane's NOUT/4 packed output words with a single buffer store.
 template <int NOUT>
@@ -1357,10 +1372,10 @@ __device__ inline void store_words(const uint32_t (&w)[NOUT / 4], __amdgpu_buffe
     __builtin_amdgcn_raw_buffer_store_b128(
         i32x4{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1]),
               static_cast<int32_t>(w[2]), static_cast<int32_t>(w[3])},
-        yr, off, 0, kStoreNT);
+        yr, off, 0, kStoreLines);
   else
     __builtin_amdgcn_raw_buffer_store_b64(
-        i32x2{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1])}, yr, off, 0, kStoreNT);
+        i32x2{static_cast<int32_t>(w[0]), static_cast<int32_t>(w[1])}, yr, off, 0, kStoreLines);
 }
 
 // Requantisation of a lane's NOUT (8 or 16) outputs, organised by stage so
