@@ -51,8 +51,8 @@ def _code_only(text: str) -> str:
 
 LAUNCH_NOTE = ("hip graph of the K steps, replayed once (value, ms_per_step: host wall clock "
                "with a synchronize on both sides; graph_event_us_per_step: HIP events around "
-               "that replay); roofline.kernel_avg_us: HIP events around a second replay of "
-               "the same graph queued behind a spin kernel, i.e. the launches' own GPU time")
+               "that replay); roofline.kernel_avg_us: HIP events around a later replay of the "
+               "same graph queued behind others, i.e. the launches' own GPU time back to back")
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -176,17 +176,18 @@ def copy_probe(nbytes: int, steps: int, warmup: int):
 
 
 def gated_graph_ms(graph, gstream, steps: int) -> float:
-    """GPU time per launch of one replay of `graph` (`steps` launches).  The
-    stream is first held by a short spin kernel (~1 ms), so the host has
-    queued the whole graph before the first event is stamped: the events
-    bracket the launches themselves, not the host-side launch of the graph,
-    which a replay timed on its own also includes (~1.3 us per step at 20
-    steps)."""
+    """GPU time per launch of one replay of `graph` (`steps` launches),
+    queued behind other replays of the same graph (about 200 launches in
+    all): the host has submitted it before the first event is stamped, so
+    the events bracket the launches back to back on a busy GPU, not the
+    host-side launch of the graph, which a replay timed on its own also
+    includes (~1 us per step at 20 steps)."""
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     with torch.cuda.stream(gstream):
-        torch.cuda._sleep(2_000_000)
+        for _ in range(max(1, 200 // steps)):
+            graph.replay()
         e0.record(gstream)
         graph.replay()
         e1.record(gstream)
