@@ -226,7 +226,8 @@ FCONV_API fconv_status fconv_plan_run(fconv_plan plan, void* stream, const fconv
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same
  * run as fconv_plan_run, with args->workspace and args->workspace_bytes
- * ignored.  The run's scratch (the repacked filter) lives in a device array
+ * ignored.  The run's scratch (the repacked filter, and for a full-size VALID
+ * filter the reduction ranges' partial sums) lives in a device array
  * of FCONV_NO_ALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
  * on until the process ends; nothing is allocated or freed per call.  Every
  * call on one GPU shares that GPU's array and leaves the last call's contents
