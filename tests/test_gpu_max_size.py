@@ -1,7 +1,7 @@
 """GPU parity at the largest tensors a plan accepts: inputs just under 2^31
 bytes (the limit of the kernels' 32-bit buffer offsets), one case per kernel
-family the benchmark layers use (row-halo 3x3, streaming 1x1, 256-pixel
-tiled stride 2 int8, tiled bf16).  The inputs are drawn on the GPU from a
+family (row-halo 3x3, streaming 1x1, 128- and 256-pixel tiled stride 2 int8,
+tiled bf16, the full-size VALID GEMM, the general kernel).  The inputs are drawn on the GPU from a
 seeded generator; the oracle cannot run whole layers of this size, so it
 computes sampled outputs one by one from their input windows (the first and
 last output pixels, the image borders, and random pixels), element by
@@ -26,6 +26,9 @@ CASES = [
     ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, None),
     ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, "256"),
     ("tile", "bf16", 28, 28, 256, 256, 3, 1, "SAME", [wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], None),
+    ("gemm", "int8", 7, 7, 512, 1024, 7, 1, "VALID", INT8_OPS, None),
+    # C = 8: the general kernel; here y (16 channels) is the tensor at the limit
+    ("general", "int8", 56, 56, 8, 16, 3, 1, "SAME", INT8_OPS, None),
 ]
 
 
@@ -50,7 +53,8 @@ def test_largest_accepted_tensors(case, monkeypatch):
         monkeypatch.setenv("FCONV_TILE_BM", bm)
     dev = torch.device("cuda:0")
     esize = 1 if dtype == "int8" else 2
-    N = LIMIT // (H * W * C * esize)
+    Ho0 = (H - 1) // stride + 1 if padding == "SAME" else (H - R) // stride + 1
+    N = LIMIT // (max(H * W * C, Ho0 * Ho0 * K) * esize)
     plan = make_plan(N, H, W, C, K, R, R, stride, padding, dtype, ops)
     assert plan.kernel_name.startswith("conv_" + family), plan.kernel_name
     Ho, Wo = plan.Ho, plan.Wo
