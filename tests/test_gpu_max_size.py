@@ -1,7 +1,9 @@
 """GPU parity at the largest tensors a plan accepts: inputs just under 2^31
 bytes (the limit of the kernels' 32-bit buffer offsets), one case per kernel
 family (row-halo 3x3, streaming 1x1, 128- and 256-pixel tiled stride 2 int8,
-tiled bf16, the full-size VALID GEMM, the general kernel).  The inputs are drawn on the GPU from a
+tiled bf16, the full-size VALID GEMM, the resident-filter and general
+kernels), and the weight gradient in bf16 and fp32.  The inputs are drawn
+on the GPU from a
 seeded generator; the oracle cannot run whole layers of this size, so it
 computes sampled outputs one by one from their input windows (the first and
 last output pixels, the image borders, and random pixels), element by
@@ -19,16 +21,17 @@ pytestmark = pytest.mark.gpu
 LIMIT = 2 ** 31 - 1  # bytes: the largest tensor a plan accepts
 
 INT8_OPS = [wl.OP_SCALE, wl.OP_SIDE, wl.OP_BIAS, wl.OP_RELU]
-# (family, dtype, H, W, C, K, R, stride, padding, ops, pinned tile height)
+# (family, dtype, H, W, C, K, R, stride, padding, ops, environment pins)
 CASES = [
-    ("halo", "int8", 56, 56, 64, 64, 3, 1, "SAME", INT8_OPS, None),
-    ("stream", "int8", 56, 56, 256, 64, 1, 1, "VALID", [wl.OP_SCALE, wl.OP_BIAS], None),
-    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, None),
-    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, "256"),
-    ("tile", "bf16", 28, 28, 256, 256, 3, 1, "SAME", [wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], None),
-    ("gemm", "int8", 7, 7, 512, 1024, 7, 1, "VALID", INT8_OPS, None),
+    ("halo", "int8", 56, 56, 64, 64, 3, 1, "SAME", INT8_OPS, {}),
+    ("stream", "int8", 56, 56, 256, 64, 1, 1, "VALID", [wl.OP_SCALE, wl.OP_BIAS], {}),
+    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {}),
+    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {"FCONV_TILE_BM": "256"}),
+    ("tile", "bf16", 28, 28, 256, 256, 3, 1, "SAME", [wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], {}),
+    ("gemm", "int8", 7, 7, 512, 1024, 7, 1, "VALID", INT8_OPS, {}),
+    ("rf", "int8", 56, 56, 64, 64, 3, 1, "SAME", INT8_OPS, {"FCONV_FORCE_VARIANT": "rf"}),
     # C = 8: the general kernel; here y (16 channels) is the tensor at the limit
-    ("general", "int8", 56, 56, 8, 16, 3, 1, "SAME", INT8_OPS, None),
+    ("general", "int8", 56, 56, 8, 16, 3, 1, "SAME", INT8_OPS, {}),
 ]
 
 
@@ -45,12 +48,12 @@ def _window(x, n, ho, wo, R, stride, pt, pl):
     return out
 
 
-@pytest.mark.parametrize("case", CASES, ids=["%s-%s%s" % (c[0], c[1], "-bm" + c[10] if c[10] else "")
-                                             for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=["%s-%s%s" % (c[0], c[1], "".join(
+    "-" + v for v in c[10].values())) for c in CASES])
 def test_largest_accepted_tensors(case, monkeypatch):
-    family, dtype, H, W, C, K, R, stride, padding, ops, bm = case
-    if bm:
-        monkeypatch.setenv("FCONV_TILE_BM", bm)
+    family, dtype, H, W, C, K, R, stride, padding, ops, pins = case
+    for k, v in pins.items():
+        monkeypatch.setenv(k, v)
     dev = torch.device("cuda:0")
     esize = 1 if dtype == "int8" else 2
     Ho0 = (H - 1) // stride + 1 if padding == "SAME" else (H - R) // stride + 1
@@ -119,3 +122,47 @@ def test_largest_accepted_tensors(case, monkeypatch):
         assert e <= TOL["bf16"], e
     del x, y, raw, ws
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_weight_gradient_largest_accepted_tensors(dtype):
+    """The weight gradient with x and dy just under 2^31 bytes (the 3x3
+    64-channel geometry): sampled dw elements against the oracle's weight
+    gradient of the one input channel and one gradient channel they involve
+    (every pixel of the batch)."""
+    dev = torch.device("cuda:0")
+    H, W, C, K, R = 56, 56, 64, 64, 3
+    esize = 2 if dtype == "bf16" else 4
+    N = LIMIT // (H * W * C * esize)
+    plan = fc_wgrad_plan(N, H, W, C, K, R, dtype)
+    say("max size wgrad %s: x %d bytes, N=%d, %s, %d B workspace" % (
+        dtype, N * H * W * C * esize, N, plan.kernel_name, plan.workspace_bytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.randn((N, H, W, C), dtype=tdt, device=dev, generator=gen)
+    dy = torch.randn((N, H, W, K), dtype=tdt, device=dev, generator=gen)
+    dw = torch.empty(plan.dw_shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    plan.run(x, dy, dw, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    taps = [(0, 0, 0, 0), (R - 1, R - 1, C - 1, K - 1), (1, 1, 0, K - 1)]
+    taps += [tuple(int(v) for v in (rng.integers(R), rng.integers(R), rng.integers(C),
+                                    rng.integers(K))) for _ in range(9)]
+    got, ref = [], []
+    for r, s, c, k in taps:
+        xc = x[..., c:c + 1].float().cpu().numpy()  # bf16 widens exactly
+        dk = dy[..., k:k + 1].float().cpu().numpy()
+        ref.append(float(oracle.wgrad(xc, dk, R, R, 1, "SAME")[r, s, 0, 0]))
+        got.append(float(dw[r, s, c, k]))
+    got, ref = np.array(got), np.array(ref)
+    e = float(np.max(np.abs(got - ref))) / float(np.max(np.abs(ref)))
+    assert e <= 1e-4, (e, got, ref)
+    del x, dy, dw, ws
+    torch.cuda.empty_cache()
+
+
+def fc_wgrad_plan(N, H, W, C, K, R, dtype):
+    import convolution_implicit_gemm_nhwc_amd as fc
+    return fc.WgradPlan(N, H, W, C, K, R, R, 1, "SAME", dtype, out_fp32=True)
