@@ -2145,6 +2145,266 @@ void conv_halo_i8_kernel(ConvArgs a) {
   }
 }
 
+// ------------------------------------------------------- row-halo, stride 2
+//
+// Stride-2 3x3 int8 convolution over 64 or 128 input channels (CS = C/64
+// k-steps of 64 bytes per tap) whose padded input rows fit 64 pixels
+// (Wo <= 31), 128 output channels per workgroup: the downsampling layers of
+// ResNet-style networks.  The tiled kernel copies a stage's filter rows and
+// patch rows into LDS for every tile and tap; here a workgroup owns
+// `halo_rows` consecutive output rows (flattened n*Ho + ho) and all 128 of its
+// channels, the filter stays in registers for the whole launch, and each step
+// (one output row) copies only the three input rows it reads.
+//
+// Waves 0-3 (one per SIMD) are MFMA waves: wave m holds the filter of packed
+// tiles 2(m&1), 2(m&1)+1 of 64-row block m>>1 (32 channels, 72*CS registers,
+// loaded straight from the packed filter) and computes both 16-pixel tiles of
+// the row (pixels past Wo read the last pixel; their results are never
+// stored), its patch fragments through a ring three k-steps deep that runs
+// into the next step's first k-steps.  Its int32 sums go through LDS to
+// epilogue waves 4-7: the hand-off of a step is a 32-pixel x 128-channel int32
+// array, 4-channel chunk k of pixel P at 16 * (k ^ (P & 31)) in P's 512 bytes
+// (conflict-free writes).  Epilogue wave e requantises pixels 8e .. 8e+7 (16
+// consecutive channels per lane, the row-halo kernel's requantisation tail)
+// and stores them whole: 1 KiB contiguous per store.
+//
+// Copies (all 1 KiB buffer->LDS, issued by the epilogue waves): step t's
+// three input rows 2*ho - pt + r (r = 0..2) of image n into row set t % 4, one
+// 64-pixel slot each, pixel X (= input column + left pad) holding its 16-byte
+// chunk c at X*C + 16*(c ^ ((X >> 1) & (4CS - 1))); rows outside the image
+// and columns past it read as zero (out-of-range offsets).  In the interval
+// that ends with the barrier after MFMA step t, each epilogue wave stores step
+// t-1, copies its side tile of step t+1 (three-slot ring) and its share of
+// step t+3's rows, then waits until only those copies (and that store) may be
+// in flight: step t+2's rows (which MFMA step t+1 prefetches from) and the side
+// tile of step t have landed.  Four row sets: steps t .. t+3 are in flight.
+constexpr int kS2Threads = 512;
+constexpr int kS2Sets = 4;      // row sets (steps t .. t+3)
+constexpr int kS2SideRing = 3;  // side-tile slots per epilogue wave
+
+template <int CS, bool SIDE, bool ORDER7, bool RELU>
+__global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void conv_halo_s2_i8_kernel(ConvArgs a) {
+  constexpr int CB = 64 * CS;      // bytes per input pixel
+  constexpr int SLOT = 64 * CB;    // one padded input row
+  constexpr int SET = 3 * SLOT;    // the three rows of a step
+  constexpr int NKS = 9 * CS;      // 64-byte k-steps
+  constexpr int D = 3;             // patch-fragment ring depth
+  constexpr int NCP = 3 * CS;      // row copies per epilogue wave per step
+  static_assert(NKS % D == 0, "ring slots must line up across steps");
+  __shared__ __attribute__((aligned(256))) char xrows[kS2Sets * SET];
+  __shared__ __attribute__((aligned(256))) char accb[2 * 16384];
+  __shared__ __attribute__((aligned(256))) char sring[SIDE ? 4 * kS2SideRing * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) float blds[256];
+  __shared__ __attribute__((aligned(16))) float clds[256];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool mfma_role = wave < 4;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+
+  const int G = gridDim.x;
+  const int bx = blockIdx.x;
+  const int b = (G % 8 == 0) ? (bx % 8) * (G / 8) + bx / 8 : bx;
+  const int rows_total = a.N * a.Ho;
+  const int g0 = b * a.halo_rows;
+  if (g0 >= rows_total) return;  // uniform per workgroup
+  const int T = min(g0 + a.halo_rows, rows_total) - g0;  // steps (output rows)
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (mfma_role) {
+    const int blk = blockIdx.y * 2 + (wave >> 1), h = wave & 1;
+    i32x4 Wf[NKS][2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+      const uint32_t row = static_cast<uint32_t>(blk * 64 + (2 * h + cg) * 16 + col);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        Wf[ks][cg] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, row * static_cast<uint32_t>(a.wrow_bytes) + ks * 64 + g * 16, 0, 0);
+    }
+    // LDS offsets of this lane's fragments inside a row slot: tile pt, tap
+    // column s, channel half c2 (the same pixels every step).
+    uint32_t ad[2][3][CS];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const int wo = min(pt * 16 + col, a.Wo - 1);
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int X = 2 * wo + s;
+#pragma unroll
+        for (int c2 = 0; c2 < CS; ++c2)
+          ad[pt][s][c2] =
+              static_cast<uint32_t>(X * CB + 16 * ((4 * c2 + g) ^ ((X >> 1) & (4 * CS - 1))));
+      }
+    }
+    auto frag = [&](int set, int pt, int ks) -> i32x4 {
+      const int tap = ks / CS, c2 = ks % CS;
+      return *reinterpret_cast<const i32x4*>(xrows + set * SET + (tap / 3) * SLOT +
+                                             ad[pt][tap % 3][c2]);
+    };
+    const i32x4 zero4 = i32x4{0, 0, 0, 0};
+    barrier();  // step 0's and step 1's rows have landed
+    i32x4 bf[D][2];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) bf[d][pt] = frag(0, pt, d);
+    for (int t = 0; t < T; ++t) {
+      const int setc = t & 3;
+      const int setn = t + 1 < T ? (t + 1) & 3 : setc;
+      i32x4 acc[2][2];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int cg = 0; cg < 2; ++cg)
+            acc[pt][cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                Wf[ks][cg], bf[ks % D][pt], ks == 0 ? zero4 : acc[pt][cg], 0, 0, 0);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+          bf[ks % D][pt] = ks + D < NKS ? frag(setc, pt, ks + D) : frag(setn, pt, ks + D - NKS);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+      }
+      char* hb = accb + (t & 1) * 16384;
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const int pix = pt * 16 + col;
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg) {
+          // channels 64*(blk % 2) + 16g + 4(2h + cg) + 0..3 of the tile's 128
+          const int chunk = 16 * ((wave >> 1) & 1) + 4 * g + 2 * h + cg;
+          *reinterpret_cast<i32x4*>(hb + pix * 512 + 16 * (chunk ^ (pix & 31))) = acc[pt][cg];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
+      barrier();
+    }
+    barrier();  // the epilogue waves' last step
+  } else {
+    const int e = wave - 4;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, static_cast<uint32_t>(a.K) * 4u);
+    const __amdgpu_buffer_rsrc_t cr =
+        make_rsrc(a.cis_vec, a.cis_vec ? static_cast<uint32_t>(a.K) * 4u : 0u);
+    // This wave's share of step u's row copies (copy k = e + 4i: row k / (4CS),
+    // KiB k % (4CS) of the slot).
+    auto copy_rows = [&](int u) {
+      const bool live = u < T;
+      const int gr = g0 + (live ? u : 0);
+      const int n = static_cast<int>(fast_div(static_cast<uint32_t>(gr), a.ho_mul, a.ho_add, a.ho_shift));
+      const int ho = gr - n * a.Ho;
+#pragma unroll
+      for (int i = 0; i < NCP; ++i) {
+        const int k = e + 4 * i;
+        const int r = k / (4 * CS);
+        const int pos = (k % (4 * CS)) * 1024 + lane * 16;
+        const int X = pos / CB;
+        const int c = ((pos % CB) >> 4) ^ ((X >> 1) & (4 * CS - 1));
+        const int hi = 2 * ho - a.pt + r, wi = X - a.pl;
+        const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                        static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+        const uint32_t src =
+            ok ? static_cast<uint32_t>(((n * a.H + hi) * a.W + wi) * CB + c * 16) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (lds_ptr_t)(xrows + (u & 3) * SET + r * SLOT + (k % (4 * CS)) * 1024), 16, src, 0,
+            0, 0);
+      }
+    };
+    // Side tile of this wave's 8 pixels at step u into ring slot u % 3.
+    auto copy_side = [&](int u) {
+      const int px = 8 * e + (lane >> 3);
+      const bool ok = u < T && px < a.Wo;
+      const uint32_t src = ok ? static_cast<uint32_t>(((g0 + u) * a.Wo + px) * a.K +
+                                                      blockIdx.y * 128 + (lane & 7) * 16)
+                              : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          sr, (lds_ptr_t)(sring + (e * kS2SideRing + u % kS2SideRing) * 1024), 16, src, 0, 0, 0);
+    };
+    copy_rows(0);
+    if (e < 2) {
+      const uint32_t off = lane < 32 ? static_cast<uint32_t>((blockIdx.y * 128 + 4 * lane) * 4)
+                                     : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(e == 0 ? br : cr, (lds_ptr_t)(e == 0 ? blds : clds),
+                                               16, off, 0, 0, 0);
+    }
+    if constexpr (SIDE) copy_side(0);
+    copy_rows(1);
+    copy_rows(2);
+    wait_vmcnt_at_most(NCP);  // step 2's rows may stay in flight
+    barrier();
+    const int px = lane >> 3, qq = lane & 7;
+    const int pix = 8 * e + px;
+    const int ch = blockIdx.y * 128 + 16 * qq;
+    float bias[16], cis_v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      bias[i] = blds[16 * qq + i];
+      cis_v[i] = a.cis_vec ? clds[16 * qq + i] : a.cis;
+    }
+    const float sis = a.sis;
+    const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
+    for (int t = 0; t <= T; ++t) {
+      if (t >= 1) {
+        const int q = t - 1;
+        const char* hb = accb + (q & 1) * 16384 + pix * 512;
+        i32x4 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i] = *reinterpret_cast<const i32x4*>(hb + 16 * ((4 * qq + i) ^ (pix & 31)));
+        i32x4 sd = i32x4{0, 0, 0, 0};
+        if constexpr (SIDE) {
+          // Landed before the barrier that ended the previous interval; read
+          // in an asm block so that the compiler adds no wait for the copies
+          // in flight into the ring's other slots.
+          const uint32_t side_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+              (lds_ptr_t)(sring + (e * kS2SideRing + q % kS2SideRing) * 1024 + lane * 16)));
+          asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                       : "=&v"(sd)
+                       : "v"(side_addr)
+                       : "memory");
+        }
+        float tv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float f = static_cast<float>(acc[i][j]);
+            tv[4 * i + j] = ORDER7 ? __builtin_fmaf(f, cis_v[4 * i + j], bias[4 * i + j])
+                                   : f * cis_v[4 * i + j];
+          }
+        uint32_t w[4];
+        halo_epilogue_tail<SIDE, ORDER7, RELU>(tv, sd, bias, sis, lo_b, hi_b, w);
+        const bool ok = pix < a.Wo;
+        const uint32_t off = ok ? static_cast<uint32_t>(((g0 + q) * a.Wo + pix) * a.K + ch)
+                                : kOutOfRange;
+        store_words<16>(w, yr, off);
+      }
+      if constexpr (SIDE) copy_side(t + 1);
+      copy_rows(t + 3);
+      // Only this interval's operations may stay in flight: step t+2's rows
+      // and the side tile of step t have landed.
+      wait_vmcnt_at_most((t >= 1 ? 1 : 0) + (SIDE ? 1 : 0) + NCP);
+      barrier();
+    }
+  }
+}
+
 // ------------------------------------------------- full-size VALID as a GEMM
 //
 // A filter as large as the image with VALID padding has a single output
@@ -2485,6 +2745,51 @@ hipError_t launch_halo(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
+template <int CS, bool SIDE, bool ORDER7>
+void launch_halo_s2_relu(dim3 g, const ConvArgs& a, hipStream_t s) {
+  if (a.relu)
+    hipLaunchKernelGGL((conv_halo_s2_i8_kernel<CS, SIDE, ORDER7, true>), g, dim3(kS2Threads), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((conv_halo_s2_i8_kernel<CS, SIDE, ORDER7, false>), g, dim3(kS2Threads), 0,
+                       s, a);
+}
+
+template <int CS>
+void launch_halo_s2_cs(dim3 g, const ConvArgs& a, hipStream_t s) {
+  if (a.use_side && a.cudnn7)
+    launch_halo_s2_relu<CS, true, true>(g, a, s);
+  else if (a.use_side)
+    launch_halo_s2_relu<CS, true, false>(g, a, s);
+  else if (a.cudnn7)
+    launch_halo_s2_relu<CS, false, true>(g, a, s);
+  else
+    launch_halo_s2_relu<CS, false, false>(g, a, s);
+}
+
+// The stride-2 row kernel: `halo_rows` output rows per workgroup (by default
+// the rows spread evenly over the CUs), 128 output channels per workgroup.
+hipError_t launch_halo_s2(const fconv_plan_s* p, const ConvArgs& a0, hipStream_t s) {
+  const fconv_desc& d = p->d;
+  if (!(d.R == 3 && d.S == 3 && d.stride_h == 2 && d.stride_w == 2 &&
+        (d.C == 64 || d.C == 128) && d.K % 128 == 0 && p->Wo <= 31))
+    return hipErrorInvalidValue;
+  ConvArgs a = a0;
+  const int cus = device_cu_count();
+  const int rows_total = d.N * p->Ho;
+  const int rows = p->halo_rows > 0 ? std::min(p->halo_rows, rows_total)
+                                    : (rows_total + cus - 1) / cus;
+  a.halo_rows = rows;
+  a.halo_rows_a = rows;
+  const dim3 g(static_cast<unsigned>((rows_total + rows - 1) / rows),
+               static_cast<unsigned>(d.K / 128));
+  if (d.C == 64)
+    launch_halo_s2_cs<1>(g, a, s);
+  else
+    launch_halo_s2_cs<2>(g, a, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_any(const fconv_plan_s* p, const void* w, void* wp, hipStream_t s) {
   switch (p->d.dtype) {
     case FCONV_INT8: return launch_pack<FCONV_INT8>(p, w, wp, s);
@@ -2554,6 +2859,7 @@ hipError_t launch_conv(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   }
   if (p->variant == kStream) return launch_stream(p, a, s);
   if (p->variant == kHalo) return launch_halo(p, a, s);
+  if (p->variant == kHaloS2) return launch_halo_s2(p, a, s);
   if (p->variant == kTiled) {
     switch (p->d.dtype) {
       case FCONV_INT8: return launch_tile<FCONV_INT8>(p, a, s);

@@ -64,13 +64,14 @@ fconv_status parse_ops(fconv_plan_s* p) {
 }
 
 const char* kernel_name(int32_t variant, int32_t dtype) {
-  static const char* names[6][3] = {
+  static const char* names[7][3] = {
       {"conv_general_i8", "conv_general_bf16", "conv_general_f32"},
       {"conv_rf_i8", "conv_rf_bf16", "conv_rf_f32"},
       {"conv_stream_i8", "conv_stream_bf16", "conv_stream_f32"},
       {"conv_tile_i8", "conv_tile_bf16", "conv_tile_f32"},
       {"conv_halo_i8", "conv_halo_bf16", "conv_halo_f32"},
-      {"conv_gemm_i8", "conv_gemm_bf16", "conv_gemm_f32"}};
+      {"conv_gemm_i8", "conv_gemm_bf16", "conv_gemm_f32"},
+      {"conv_halo_s2_i8", "conv_halo_s2_bf16", "conv_halo_s2_f32"}};
   return names[variant][dtype];
 }
 
@@ -85,11 +86,22 @@ bool gemm_shape(const fconv_plan_s* p) {
          static_cast<int64_t>(p->pack_bytes) < (int64_t{1} << 31);
 }
 
+// The stride-2 row kernel: int8, 3x3, stride 2, 64 or 128 input channels,
+// 128-channel output slices, padded input rows of at most 64 pixels (Wo <= 31),
+// in 32-bit buffer extents.
+bool halo_s2_shape(const fconv_plan_s* p) {
+  const fconv_desc& d = p->d;
+  return d.dtype == FCONV_INT8 && d.R == 3 && d.S == 3 && d.stride_h == 2 && d.stride_w == 2 &&
+         (d.C == 64 || d.C == 128) && d.K % 128 == 0 && p->Wo <= 31 &&
+         p->x_elems < (int64_t{1} << 31) && p->y_elems < (int64_t{1} << 31) &&
+         static_cast<int64_t>(p->pack_bytes) < (int64_t{1} << 31);
+}
+
 // LDS budget of the resident-filter kernel's 64-row filter slice: at most
 // this much, so that two workgroups still fit in a CU's 160 KiB.
 constexpr int64_t kRfMaxLds = 80 * 1024;
 
-// Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream|gemm
+// Kernel choice.  FCONV_FORCE_VARIANT=general|rf|tile|stream|gemm|halo_s2
 // (environment) pins a kernel family where the shape allows it, for A/B
 // comparisons (a full-size VALID filter takes the GEMM kernel unless another
 // family is pinned);
@@ -171,12 +183,21 @@ void choose_variant(fconv_plan_s* p) {
       if (hr && atoi(hr) > 0) p->halo_rows = atoi(hr);
     }
   }
+  // 3x3 stride 2 over 64 or 128 channels: the stride-2 row kernel, unless
+  // another family is asked for by name.
+  if (halo_s2_shape(p) && (!force || strcmp(force, "halo_s2") == 0)) {
+    p->variant = kHaloS2;
+    p->pixel_tiles = 1;
+    p->ring_depth = 0;
+    const char* hr = getenv("FCONV_HALO_ROWS");
+    if (hr && atoi(hr) > 0) p->halo_rows = atoi(hr);
+  }
   p->kernel_name = kernel_name(p->variant, d.dtype);
 }
 
 // Shape conditions of each family, as choose_variant applies them.
 struct FamilyFit {
-  bool rf, tile, stream, halo, gemm;
+  bool rf, tile, stream, halo, gemm, halo_s2;
 };
 
 FamilyFit family_fit(const fconv_plan_s* p) {
@@ -197,6 +218,7 @@ FamilyFit family_fit(const fconv_plan_s* p) {
   f.halo = f.stream && d.R == 3 && d.S == 3 && cs == 1 && d.stride_h == 1 && d.stride_w == 1 &&
            d.W + p->pl + p->pr <= 64;
   f.gemm = gemm_shape(p);
+  f.halo_s2 = halo_s2_shape(p);
   return f;
 }
 
@@ -276,6 +298,7 @@ int list_configs(const fconv_plan_s* p, KernelConfig* out, int max) {
   const FamilyFit f = family_fit(p);
   if (f.gemm) add(kGemm, 0, 0, 0);
   if (f.halo) add(kHalo, 1, 0, 0);
+  if (f.halo_s2) add(kHaloS2, 1, 0, 0);
   if (f.stream) add(kStream, 1, 0, 0);
   if (f.tile) {
     add(kTiled, 0, 0, 0);

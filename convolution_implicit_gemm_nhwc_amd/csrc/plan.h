@@ -18,6 +18,7 @@ enum Variant : int32_t {
   kTiled = 3,          // 128x128 LDS-tiled implicit GEMM, long reductions
   kHalo = 4,           // int8 stride 1 over 64 channels: input rows staged in LDS
   kGemm = 5,           // full-size VALID filter: split-reduction GEMM + sum/epilogue
+  kHaloS2 = 6,         // int8 3x3 stride 2 over 64/128 channels: filter in registers, rows in LDS
 };
 
 // Division by a runtime constant d for numerators below 2^31:

@@ -12,7 +12,8 @@ from gpu_helpers import TOL, device, float_error, from_dev, make_plan, oracle_ou
 
 pytestmark = pytest.mark.gpu
 
-FAMILIES = ("conv_halo_", "conv_stream_", "conv_tile_", "conv_rf_", "conv_general_")
+FAMILIES = ("conv_halo_", "conv_stream_", "conv_tile_", "conv_rf_", "conv_general_",
+            "conv_halo_s2_")
 
 
 @pytest.mark.parametrize("name", ["resnet_3x3_int8", "resnet_1x1_int8", "resnet_3x3s2_int8",

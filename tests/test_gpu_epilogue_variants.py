@@ -43,14 +43,14 @@ def _check(name, N, per_channel, order, variant=None, monkeypatch=None, expect=N
 
 @pytest.mark.parametrize("name,expect", [
     ("resnet_3x3_int8", ("conv_halo_i8",)), ("resnet_1x1_int8", ("conv_stream_i8",)),
-    ("resnet_3x3s2_int8", ("conv_tile_i8",)), ("tiny_int8_3x3", ("conv_general_i8",))])
+    ("resnet_3x3s2_int8", ("conv_halo_s2_i8",)), ("tiny_int8_3x3", ("conv_general_i8",))])
 def test_per_channel_scale(name, expect):
     _check(name, 4, True, 8, expect=expect)
 
 
 @pytest.mark.parametrize("name,variant", [
     ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"), ("resnet_3x3_int8", "stream"),
-    ("resnet_1x1_int8", "tile")])
+    ("resnet_1x1_int8", "tile"), ("resnet_3x3s2_int8", "tile")])
 def test_per_channel_scale_forced_variant(name, variant, monkeypatch):
     _check(name, 2, True, 8, variant, monkeypatch, expect=("conv_%s_i8" % variant,))
 
@@ -58,14 +58,14 @@ def test_per_channel_scale_forced_variant(name, variant, monkeypatch):
 @pytest.mark.parametrize("per_channel", [False, True])
 @pytest.mark.parametrize("name,expect", [
     ("resnet_3x3_int8", ("conv_halo_i8",)), ("resnet_1x1_int8", ("conv_stream_i8",)),
-    ("resnet_3x3s2_int8", ("conv_tile_i8",)), ("tiny_int8_3x3", ("conv_general_i8",))])
+    ("resnet_3x3s2_int8", ("conv_halo_s2_i8",)), ("tiny_int8_3x3", ("conv_general_i8",))])
 def test_cudnn7_order(name, expect, per_channel):
     _check(name, 4, per_channel, 7, expect=expect)
 
 
 @pytest.mark.parametrize("name,variant", [
     ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"), ("resnet_3x3_int8", "stream"),
-    ("resnet_1x1_int8", "tile"), ("resnet_3x3s2_int8", "general")])
+    ("resnet_1x1_int8", "tile"), ("resnet_3x3s2_int8", "general"), ("resnet_3x3s2_int8", "tile")])
 def test_cudnn7_order_forced_variant(name, variant, monkeypatch):
     _check(name, 2, True, 7, variant, monkeypatch, expect=("conv_%s_i8" % variant,))
 

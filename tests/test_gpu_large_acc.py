@@ -66,9 +66,11 @@ FAMILIES = [
     ("halo", (3, 10, 12, 64, 64, 3, 1, "SAME"), None, None),
     ("stream", (2, 9, 11, 512, 64, 1, 1, "VALID"), None, None),
     ("stream", (3, 10, 12, 64, 64, 3, 1, "SAME"), "stream", None),
-    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), None, "64"),
-    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), None, "128"),
-    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), None, "256"),
+    ("halo_s2", (3, 15, 15, 128, 128, 3, 2, "SAME"), None, None),
+    ("halo_s2", (3, 15, 15, 64, 128, 3, 2, "SAME"), None, None),
+    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), "tile", "64"),
+    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), "tile", "128"),
+    ("tile", (3, 15, 15, 128, 128, 3, 2, "SAME"), "tile", "256"),
     ("tile", (2, 9, 13, 128, 64, 3, 1, "SAME"), "tile", None),
     ("tile", (2, 7, 9, 1152, 64, 1, 1, "VALID"), None, None),
     ("rf", (3, 15, 15, 128, 128, 3, 2, "SAME"), "rf", None),

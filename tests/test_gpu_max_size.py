@@ -1,6 +1,7 @@
 """GPU parity at the largest tensors a plan accepts: inputs just under 2^31
 bytes (the limit of the kernels' 32-bit buffer offsets), one case per kernel
-family (row-halo 3x3, streaming 1x1, 128- and 256-pixel tiled stride 2 int8,
+family (row-halo 3x3, streaming 1x1, the stride-2 row kernel, 128- and 256-pixel
+tiled stride 2 int8,
 tiled bf16, the full-size VALID GEMM, the resident-filter and general
 kernels), and the weight gradient in bf16 and fp32.  The inputs are drawn
 on the GPU from a
@@ -25,8 +26,10 @@ INT8_OPS = [wl.OP_SCALE, wl.OP_SIDE, wl.OP_BIAS, wl.OP_RELU]
 CASES = [
     ("halo", "int8", 56, 56, 64, 64, 3, 1, "SAME", INT8_OPS, {}),
     ("stream", "int8", 56, 56, 256, 64, 1, 1, "VALID", [wl.OP_SCALE, wl.OP_BIAS], {}),
-    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {}),
-    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {"FCONV_TILE_BM": "256"}),
+    ("halo_s2", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {}),
+    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS, {"FCONV_FORCE_VARIANT": "tile"}),
+    ("tile", "int8", 56, 56, 128, 128, 3, 2, "SAME", INT8_OPS,
+     {"FCONV_FORCE_VARIANT": "tile", "FCONV_TILE_BM": "256"}),
     ("tile", "bf16", 28, 28, 256, 256, 3, 1, "SAME", [wl.OP_BIAS, wl.OP_BN, wl.OP_RELU], {}),
     ("gemm", "int8", 7, 7, 512, 1024, 7, 1, "VALID", INT8_OPS, {}),
     ("rf", "int8", 56, 56, 64, 64, 3, 1, "SAME", INT8_OPS, {"FCONV_FORCE_VARIANT": "rf"}),

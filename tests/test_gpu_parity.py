@@ -309,10 +309,52 @@ def test_halo_shapes(N, H, W, K, pad, side, rows, monkeypatch):
     assert np.array_equal(y, r), "%d differ" % np.count_nonzero(y != r)
 
 
+@pytest.mark.parametrize("N,H,W,C,K,pad,side,relu,rows", [
+    (5, 9, 9, 128, 128, "SAME", True, True, 0),      # odd size: top and left pad 1
+    (3, 8, 10, 64, 128, "SAME", True, True, 0),      # 64 channels, top pad 0
+    (2, 62, 62, 128, 256, "SAME", True, False, 0),   # Wo = 31 (widest), two channel slices
+    (7, 11, 6, 128, 128, "VALID", True, True, 0),    # VALID, Wo = 2
+    (4, 1, 1, 64, 128, "SAME", False, True, 0),      # 1x1 images: all but one tap in padding
+    (300, 3, 3, 128, 128, "SAME", True, True, 0),    # Ho = 2: workgroups span many images
+    (6, 13, 13, 128, 128, "SAME", True, False, 5),   # forced 5 rows per workgroup, no ReLU
+    (4, 16, 16, 64, 128, "SAME", True, True, 13),    # forced 13 rows: ragged last workgroup
+])
+def test_halo_s2_shapes(N, H, W, C, K, pad, side, relu, rows, monkeypatch):
+    """The stride-2 row kernel's edge cases: both SAME paddings of stride 2
+    (top/left 0 or 1), VALID, images smaller than the filter, workgroups whose
+    rows span images, ragged last workgroups, both channel counts, with and
+    without the side input and ReLU."""
+    if rows:
+        monkeypatch.setenv("FCONV_HALO_ROWS", str(rows))
+    rng = np.random.default_rng(N * 1000 + H * 10 + C + K)
+    Ho, Wo = oracle.geometry(H, W, 3, 3, 2, 2, pad == "SAME")[:2]
+    x = wl.draw_int8(rng, (N, H, W, C), -128, 127)
+    w = wl.draw_int8(rng, (3, 3, C, K), -128, 127)
+    sd = wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if side else None
+    ops = [wl.OP_SCALE] + ([wl.OP_SIDE] if side else []) + [wl.OP_BIAS] + (
+        [wl.OP_RELU] if relu else [])
+    c = dict(shape=(N, H, W, C, K, 3, 3, 2, pad), x=x, w=w,
+             bias=rng.normal(0, 40, K).astype(np.float32), side=sd,
+             cis=np.float32(2.0 ** -11), sis=np.float32(0.5 if side else 0.0), relu=relu,
+             ops=ops, bn=None, use_bias=True)
+    say("halo_s2 shape %s side=%s relu=%s rows=%d" % (c["shape"], side, relu, rows))
+    y, r, guards, plan = _run_case(c, "int8")
+    assert plan.kernel_name == "conv_halo_s2_i8", plan.kernel_name
+    assert guards
+    assert np.array_equal(y, r), "%d differ" % np.count_nonzero(y != r)
+
+
+def test_halo_s2_falls_back_past_31_output_columns():
+    """Wo = 32 needs a 65-pixel input row: the tiled kernel takes it."""
+    plan = make_plan(1, 4, 64, 128, 128, 3, 3, 2, "SAME", "int8",
+                     [wl.OP_SCALE, wl.OP_BIAS, wl.OP_RELU])
+    assert plan.Wo == 32 and plan.kernel_name == "conv_tile_i8", plan.kernel_name
+
+
 @pytest.mark.parametrize("name,variant", [
     ("resnet_3x3_int8", "general"), ("resnet_3x3_int8", "rf"), ("resnet_3x3_int8", "stream"),
     ("resnet_1x1_int8", "general"), ("resnet_1x1_int8", "rf"), ("resnet_1x1_int8", "tile"),
-    ("resnet_3x3s2_int8", "general"), ("resnet_3x3s2_int8", "rf")])
+    ("resnet_3x3s2_int8", "general"), ("resnet_3x3s2_int8", "rf"), ("resnet_3x3s2_int8", "tile")])
 def test_workload_forced_variant(name, variant, monkeypatch):
     """Every kernel family stays bit-exact on the layers another family is
     normally chosen for (FCONV_FORCE_VARIANT is read at plan creation; the
