@@ -2154,46 +2154,71 @@ void conv_halo_i8_kernel(ConvArgs a) {
 // patch rows into LDS for every tile and tap; here a workgroup owns
 // `halo_rows` consecutive output rows (flattened n*Ho + ho) and all 128 of its
 // channels, the filter stays in registers for the whole launch, and each step
-// (one output row) copies only the three input rows it reads.
+// (one output row) copies only the input rows it does not share with the
+// previous step: two, or three at the first row of an image.
 //
-// Waves 0-3 (one per SIMD) are MFMA waves: wave m holds the filter of packed
-// tiles 2(m&1), 2(m&1)+1 of 64-row block m>>1 (32 channels, 72*CS registers,
-// loaded straight from the packed filter) and computes both 16-pixel tiles of
-// the row (pixels past Wo read the last pixel; their results are never
-// stored), its patch fragments through a ring three k-steps deep that runs
-// into the next step's first k-steps.  Its int32 sums go through LDS to
-// epilogue waves 4-7: the hand-off of a step is a 32-pixel x 128-channel int32
-// array, 4-channel chunk k of pixel P at 16 * (k ^ (P & 31)) in P's 512 bytes
-// (conflict-free writes).  Epilogue wave e requantises pixels 8e .. 8e+7 (16
+// Waves 0-3 (one per SIMD) are MFMA waves.  Each holds a share of the
+// 128-channel filter slice in registers (loaded straight from the packed
+// filter): over 64 channels (CS = 1) wave m holds packed tiles 2(m&1),
+// 2(m&1)+1 of 64-row block m>>1 (32 channels, all 9 k-steps); over 128
+// channels (CS = 2) it holds all four tiles of block m>>1 and half of the 18
+// k-steps, (m&1)*9 .. (m&1)*9+8 (64 channels: each patch fragment read from
+// LDS feeds four MFMAs).  Each wave computes both 16-pixel tiles of the row
+// (pixels past Wo read the last pixel; their results are never stored), one
+// tile after the other, so that the first tile's sums go to LDS while the
+// second tile's MFMAs run; its patch fragments come through a ring three
+// fragments deep that runs into the next step's first fragments.  The int32
+// sums go through LDS to epilogue waves 4-7: per step and per k-step half a
+// 32-pixel x 128-channel int32 array, 4-channel chunk k of pixel P at
+// 16 * (k ^ (P & 31)) in P's 512 bytes (conflict-free writes).  Epilogue wave
+// e adds the halves (exact int32), requantises pixels 8e .. 8e+7 (16
 // consecutive channels per lane, the row-halo kernel's requantisation tail)
 // and stores them whole: 1 KiB contiguous per store.
 //
-// Copies (all 1 KiB buffer->LDS, issued by the epilogue waves): step t's
-// three input rows 2*ho - pt + r (r = 0..2) of image n into row set t % 4, one
-// 64-pixel slot each, pixel X (= input column + left pad) holding its 16-byte
-// chunk c at X*C + 16*(c ^ ((X >> 1) & (4CS - 1))); rows outside the image
-// and columns past it read as zero (out-of-range offsets).  In the interval
-// that ends with the barrier after MFMA step t, each epilogue wave stores step
-// t-1, copies its side tile of step t+1 (three-slot ring) and its share of
-// step t+3's rows, then waits until only those copies (and that store) may be
-// in flight: step t+2's rows (which MFMA step t+1 prefetches from) and the side
-// tile of step t have landed.  Four row sets: steps t .. t+3 are in flight.
+// Input rows (1 KiB buffer->LDS copies, issued by the epilogue waves) live in
+// a ring of nine 64-pixel slots.  The workgroup's rows are numbered in the
+// order its steps first need them (row r of step u is number k0(u) + r, with
+// k0 advancing by 2 per output row and by 3 more at each image change), and
+// row number k sits in slot k % 9: the rows of three consecutive steps span
+// at most nine numbers, so a copy never lands on a row still being read.
+// Even pixels (X = input column + left pad) fill a slot's first 32 pixel places
+// and odd pixels the rest, so a tap's 16 pixels (stride 2) are consecutive
+// places, P = (X & 1) * 32 + X / 2; place P holds its 16-byte chunk c at
+// P*C + 16*(c ^ ((P >> 1) & (4CS - 1))), conflict-free for 16 consecutive
+// places.  Rows outside the image and columns past it read as zero
+// (out-of-range offsets).  In the interval that ends with the barrier after
+// MFMA step t, each epilogue wave copies its share of step t+2's new rows and
+// its side tile of step t+1 (three-slot ring), requantises and stores step
+// t-1, then waits for its copies (the store may stay in flight): MFMA step t+1
+// reads rows that were waited for one interval earlier, and the prefetch at
+// the end of MFMA step t reads only rows published before it.
 constexpr int kS2Threads = 512;
-constexpr int kS2Sets = 4;      // row sets (steps t .. t+3)
+constexpr int kS2Slots = 9;     // input-row slots
 constexpr int kS2SideRing = 3;  // side-tile slots per epilogue wave
+
+// Row number of row 0 of the workgroup's step for flattened output row gr
+// (the workgroup starts at output row ho0 of image n0).
+__device__ inline int halo_s2_k0(const ConvArgs& a, int gr, int n0, int ho0) {
+  const int n = static_cast<int>(fast_div(static_cast<uint32_t>(gr), a.ho_mul, a.ho_add, a.ho_shift));
+  const int ho = gr - n * a.Ho;
+  if (n == n0) return 2 * (ho - ho0);
+  return 2 * (a.Ho - 1 - ho0) + 3 + (n - n0 - 1) * (2 * (a.Ho - 1) + 3) + 2 * ho;
+}
 
 template <int CS, bool SIDE, bool ORDER7, bool RELU>
 __global__ __launch_bounds__(kS2Threads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void conv_halo_s2_i8_kernel(ConvArgs a) {
   constexpr int CB = 64 * CS;      // bytes per input pixel
   constexpr int SLOT = 64 * CB;    // one padded input row
-  constexpr int SET = 3 * SLOT;    // the three rows of a step
-  constexpr int NKS = 9 * CS;      // 64-byte k-steps
+  constexpr int KSPLIT = CS;       // k-step parts (one sum array each)
+  constexpr int NT = 2 * CS;       // 16-channel tiles per MFMA wave
+  constexpr int NK = 9;            // k-steps per MFMA wave
+  constexpr int NF = 2 * NK;       // fragments per step (two pixel tiles)
   constexpr int D = 3;             // patch-fragment ring depth
-  constexpr int NCP = 3 * CS;      // row copies per epilogue wave per step
-  static_assert(NKS % D == 0, "ring slots must line up across steps");
-  __shared__ __attribute__((aligned(256))) char xrows[kS2Sets * SET];
-  __shared__ __attribute__((aligned(256))) char accb[2 * 16384];
+  constexpr int HSZ = 16384;       // one 32-pixel x 128-channel int32 array
+  static_assert(NF % D == 0, "ring slots must line up across steps");
+  __shared__ __attribute__((aligned(256))) char xrows[kS2Slots * SLOT];
+  __shared__ __attribute__((aligned(256))) char accb[2 * KSPLIT * HSZ];
   __shared__ __attribute__((aligned(256))) char sring[SIDE ? 4 * kS2SideRing * 1024 : 16];
   __shared__ __attribute__((aligned(16))) float blds[256];
   __shared__ __attribute__((aligned(16))) float clds[256];
@@ -2211,6 +2236,8 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
   const int g0 = b * a.halo_rows;
   if (g0 >= rows_total) return;  // uniform per workgroup
   const int T = min(g0 + a.halo_rows, rows_total) - g0;  // steps (output rows)
+  const int n0 = static_cast<int>(fast_div(static_cast<uint32_t>(g0), a.ho_mul, a.ho_add, a.ho_shift));
+  const int ho0 = g0 - n0 * a.Ho;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, SIDE ? a.side_bytes : 0u);
@@ -2224,16 +2251,8 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
   };
 
   if (mfma_role) {
-    const int blk = blockIdx.y * 2 + (wave >> 1), h = wave & 1;
-    i32x4 Wf[NKS][2];
-#pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
-      const uint32_t row = static_cast<uint32_t>(blk * 64 + (2 * h + cg) * 16 + col);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        Wf[ks][cg] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, row * static_cast<uint32_t>(a.wrow_bytes) + ks * 64 + g * 16, 0, 0);
-    }
+    const int blk = blockIdx.y * 2 + (wave >> 1);
+    const int j0 = CS == 1 ? 2 * (wave & 1) : 0;  // first packed tile of the wave
     // LDS offsets of this lane's fragments inside a row slot: tile pt, tap
     // column s, channel half c2 (the same pixels every step).
     uint32_t ad[2][3][CS];
@@ -2243,87 +2262,131 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         const int X = 2 * wo + s;
+        const int P = (X & 1) * 32 + (X >> 1);
 #pragma unroll
         for (int c2 = 0; c2 < CS; ++c2)
           ad[pt][s][c2] =
-              static_cast<uint32_t>(X * CB + 16 * ((4 * c2 + g) ^ ((X >> 1) & (4 * CS - 1))));
+              static_cast<uint32_t>(P * CB + 16 * ((4 * c2 + g) ^ ((P >> 1) & (4 * CS - 1))));
       }
     }
-    auto frag = [&](int set, int pt, int ks) -> i32x4 {
-      const int tap = ks / CS, c2 = ks % CS;
-      return *reinterpret_cast<const i32x4*>(xrows + set * SET + (tap / 3) * SLOT +
-                                             ad[pt][tap % 3][c2]);
-    };
     const i32x4 zero4 = i32x4{0, 0, 0, 0};
-    barrier();  // step 0's and step 1's rows have landed
-    i32x4 bf[D][2];
+    // The wave's k-steps kh*NK .. kh*NK + NK - 1 (kh fixed at compile time so
+    // that every register index is static).
+    auto run = [&](auto khc) {
+      constexpr int kh = decltype(khc)::value;
+      i32x4 Wf[NK][NT];
 #pragma unroll
-    for (int d = 0; d < D; ++d)
+      for (int jj = 0; jj < NT; ++jj) {
+        const uint32_t row = static_cast<uint32_t>(blk * 64 + (j0 + jj) * 16 + col);
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) bf[d][pt] = frag(0, pt, d);
-    for (int t = 0; t < T; ++t) {
-      const int setc = t & 3;
-      const int setn = t + 1 < T ? (t + 1) & 3 : setc;
-      i32x4 acc[2][2];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-          for (int cg = 0; cg < 2; ++cg)
-            acc[pt][cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                Wf[ks][cg], bf[ks % D][pt], ks == 0 ? zero4 : acc[pt][cg], 0, 0, 0);
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-          bf[ks % D][pt] = ks + D < NKS ? frag(setc, pt, ks + D) : frag(setn, pt, ks + D - NKS);
+        for (int kk = 0; kk < NK; ++kk)
+          Wf[kk][jj] = __builtin_amdgcn_raw_buffer_load_b128(
+              wr, row * static_cast<uint32_t>(a.wrow_bytes) + (kh * NK + kk) * 64 + g * 16, 0, 0);
       }
+      // Fragment f of a step (pixel tile f / NK, k-step f % NK) from the row
+      // slots rb[r] (byte offsets) of that step.
+      auto frag = [&](const uint32_t (&rb)[3], int f) -> i32x4 {
+        const int pt = f / NK, ks = kh * NK + f % NK;
+        const int tap = ks / CS, c2 = ks % CS;
+        return *reinterpret_cast<const i32x4*>(xrows + rb[tap / 3] + ad[pt][tap % 3][c2]);
+      };
+      auto slots = [&](int u, uint32_t (&rb)[3]) {
+        const int k0 = halo_s2_k0(a, g0 + u, n0, ho0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-      }
-      char* hb = accb + (t & 1) * 16384;
+        for (int r = 0; r < 3; ++r)
+          rb[r] = static_cast<uint32_t>(((k0 + r) % kS2Slots) * SLOT);
+      };
+      uint32_t rc[3], rn[3];
+      slots(0, rc);
+      barrier();  // steps 0 and 1's rows have landed
+      i32x4 bf[D];
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const int pix = pt * 16 + col;
+      for (int d = 0; d < D; ++d) bf[d] = frag(rc, d);
+      for (int t = 0; t < T; ++t) {
+        slots(t + 1 < T ? t + 1 : t, rn);
+        char* hb = accb + ((t & 1) * KSPLIT + kh) * HSZ;
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg) {
-          // channels 64*(blk % 2) + 16g + 4(2h + cg) + 0..3 of the tile's 128
-          const int chunk = 16 * ((wave >> 1) & 1) + 4 * g + 2 * h + cg;
-          *reinterpret_cast<i32x4*>(hb + pix * 512 + 16 * (chunk ^ (pix & 31))) = acc[pt][cg];
+        for (int pt = 0; pt < 2; ++pt) {
+          i32x4 acc[NT];
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) {
+            const int f = pt * NK + kk;
+#pragma unroll
+            for (int jj = 0; jj < NT; ++jj)
+              acc[jj] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Wf[kk][jj], bf[f % D],
+                                                              kk == 0 ? zero4 : acc[jj], 0, 0, 0);
+            bf[f % D] = f + D < NF ? frag(rc, f + D) : frag(rn, f + D - NF);
+          }
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          }
+          // This tile's sums: channels 64*(blk % 2) + 16g + 4(j0 + jj) + 0..3
+          // of the workgroup's 128 (the first tile's writes overlap the
+          // second tile's MFMAs).
+          const int pix = pt * 16 + col;
+#pragma unroll
+          for (int jj = 0; jj < NT; ++jj) {
+            const int chunk = 16 * ((wave >> 1) & 1) + 4 * g + j0 + jj;
+            *reinterpret_cast<i32x4*>(hb + pix * 512 + 16 * (chunk ^ (pix & 31))) = acc[jj];
+          }
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
+        barrier();
+#pragma unroll
+        for (int r = 0; r < 3; ++r) rc[r] = rn[r];
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): hand-off written
-      barrier();
+      barrier();  // the epilogue waves' last step
+    };
+    if constexpr (CS == 2) {
+      if (wave & 1)
+        run(std::integral_constant<int, 1>{});
+      else
+        run(std::integral_constant<int, 0>{});
+    } else {
+      run(std::integral_constant<int, 0>{});
     }
-    barrier();  // the epilogue waves' last step
   } else {
     const int e = wave - 4;
     const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, static_cast<uint32_t>(a.K) * 4u);
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(a.cis_vec, a.cis_vec ? static_cast<uint32_t>(a.K) * 4u : 0u);
-    // This wave's share of step u's row copies (copy k = e + 4i: row k / (4CS),
-    // KiB k % (4CS) of the slot).
+    // This wave copies KiB e + 4c (c < CS) of every row: the source offset
+    // inside the row, per lane (out-of-range columns get 2^31, which keeps
+    // the sum with any row's offset, below 2^31, out of range).
+    // (A fixed bound: with a bound that depends on CS, captured by the lambda
+    // below, clang's host pass drops the kernel's launch stub.)
+    uint32_t lane_off[2];
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+      const int pos = (e + 4 * c) * 1024 + lane * 16;
+      const int P = pos / CB;
+      const int X = P < 32 ? 2 * P : 2 * (P - 32) + 1;
+      const int ch = ((pos % CB) >> 4) ^ ((P >> 1) & (4 * CS - 1));
+      const int wi = X - a.pl;
+      lane_off[c] = static_cast<unsigned>(wi) < static_cast<unsigned>(a.W)
+                        ? static_cast<uint32_t>(wi * CB + ch * 16)
+                        : kOutOfRange;
+    }
+    // This wave's share of step u's new rows (all three at the first step and
+    // at the first row of an image, else rows 1 and 2).
     auto copy_rows = [&](int u) {
-      const bool live = u < T;
-      const int gr = g0 + (live ? u : 0);
+      if (u >= T) return;
+      const int gr = g0 + u;
       const int n = static_cast<int>(fast_div(static_cast<uint32_t>(gr), a.ho_mul, a.ho_add, a.ho_shift));
       const int ho = gr - n * a.Ho;
+      const int k0 = halo_s2_k0(a, gr, n0, ho0);
+      for (int r = (u == 0 || ho == 0) ? 0 : 1; r < 3; ++r) {
+        const int hi = 2 * ho - a.pt + r;
+        const bool row_ok = static_cast<unsigned>(hi) < static_cast<unsigned>(a.H);
+        const uint32_t rbase = static_cast<uint32_t>((n * a.H + hi) * a.W * CB);
+        char* slot = xrows + ((k0 + r) % kS2Slots) * SLOT;
 #pragma unroll
-      for (int i = 0; i < NCP; ++i) {
-        const int k = e + 4 * i;
-        const int r = k / (4 * CS);
-        const int pos = (k % (4 * CS)) * 1024 + lane * 16;
-        const int X = pos / CB;
-        const int c = ((pos % CB) >> 4) ^ ((X >> 1) & (4 * CS - 1));
-        const int hi = 2 * ho - a.pt + r, wi = X - a.pl;
-        const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
-                        static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
-        const uint32_t src =
-            ok ? static_cast<uint32_t>(((n * a.H + hi) * a.W + wi) * CB + c * 16) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            xr, (lds_ptr_t)(xrows + (u & 3) * SET + r * SLOT + (k % (4 * CS)) * 1024), 16, src, 0,
-            0, 0);
+        for (int c = 0; c < CS; ++c)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(slot + (e + 4 * c) * 1024), 16,
+                                                   row_ok ? rbase + lane_off[c] : kOutOfRange, 0,
+                                                   0, 0);
       }
     };
     // Side tile of this wave's 8 pixels at step u into ring slot u % 3.
@@ -2337,6 +2400,7 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
           sr, (lds_ptr_t)(sring + (e * kS2SideRing + u % kS2SideRing) * 1024), 16, src, 0, 0, 0);
     };
     copy_rows(0);
+    copy_rows(1);
     if (e < 2) {
       const uint32_t off = lane < 32 ? static_cast<uint32_t>((blockIdx.y * 128 + 4 * lane) * 4)
                                      : kOutOfRange;
@@ -2344,9 +2408,7 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
                                                16, off, 0, 0, 0);
     }
     if constexpr (SIDE) copy_side(0);
-    copy_rows(1);
-    copy_rows(2);
-    wait_vmcnt_at_most(NCP);  // step 2's rows may stay in flight
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): steps 0 and 1 are read during step 0
     barrier();
     const int px = lane >> 3, qq = lane & 7;
     const int pix = 8 * e + px;
@@ -2360,13 +2422,18 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
     const float sis = a.sis;
     const float lo_b = kRoundMagic + (a.relu ? 0.0f : -128.0f), hi_b = kRoundMagic + 127.0f;
     for (int t = 0; t <= T; ++t) {
+      copy_rows(t + 2);
+      if constexpr (SIDE) copy_side(t + 1);
       if (t >= 1) {
         const int q = t - 1;
-        const char* hb = accb + (q & 1) * 16384 + pix * 512;
         i32x4 acc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i] = *reinterpret_cast<const i32x4*>(hb + 16 * ((4 * qq + i) ^ (pix & 31)));
+        for (int i = 0; i < 4; ++i) {
+          const int off = pix * 512 + 16 * ((4 * qq + i) ^ (pix & 31));
+          acc[i] = *reinterpret_cast<const i32x4*>(accb + (q & 1) * KSPLIT * HSZ + off);
+          if constexpr (KSPLIT == 2)
+            acc[i] += *reinterpret_cast<const i32x4*>(accb + ((q & 1) * KSPLIT + 1) * HSZ + off);
+        }
         i32x4 sd = i32x4{0, 0, 0, 0};
         if constexpr (SIDE) {
           // Landed before the barrier that ended the previous interval; read
@@ -2394,12 +2461,11 @@ void conv_halo_s2_i8_kernel(ConvArgs a) {
         const uint32_t off = ok ? static_cast<uint32_t>(((g0 + q) * a.Wo + pix) * a.K + ch)
                                 : kOutOfRange;
         store_words<16>(w, yr, off);
+        // This interval's copies have landed (the store may stay in flight).
+        __builtin_amdgcn_s_waitcnt(0x0f71);  // vmcnt(1)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
       }
-      if constexpr (SIDE) copy_side(t + 1);
-      copy_rows(t + 3);
-      // Only this interval's operations may stay in flight: step t+2's rows
-      // and the side tile of step t have landed.
-      wait_vmcnt_at_most((t >= 1 ? 1 : 0) + (SIDE ? 1 : 0) + NCP);
       barrier();
     }
   }
