@@ -2604,6 +2604,18 @@ __global__ __launch_bounds__(kGemmReduceThreads) void conv_gemm_reduce_kernel(Co
   if (ch0 >= a.K) return;
   const int64_t tile_stride = static_cast<int64_t>(a.N) * a.Kp * 4;  // bytes of one range's tiles
   const char* src = static_cast<const char*>(a.part) + (static_cast<int64_t>(n) * a.Kp + ch0) * 4;
+  // The epilogue's per-channel values and side chunk first: their loads do
+  // not depend on the sums, so they are in flight with the partial tiles'.
+  i32x4 sc = i32x4{0, 0, 0, 0};
+  float bias[8], cis[8];
+  FloatEpiParams<8> P;
+  if constexpr (DT == FCONV_INT8) {
+    if (a.use_side) sc = load_side_chunk<8>(a, n, ch0, KVEC);
+    load_bias<8>(a, ch0, KVEC, bias);
+    load_scales<8>(a, ch0, KVEC, cis);
+  } else {
+    P.load(a, ch0, KVEC);
+  }
   Acc s0 = Acc{0, 0, 0, 0}, s1 = Acc{0, 0, 0, 0};
   for (int sp0 = 0; sp0 < a.gemm_splits; sp0 += 8) {
     Acc v0[8], v1[8];
@@ -2629,12 +2641,10 @@ __global__ __launch_bounds__(kGemmReduceThreads) void conv_gemm_reduce_kernel(Co
     v[e] = s0[e];
     v[4 + e] = s1[e];
   }
-  if constexpr (DT == FCONV_INT8) {
-    const i32x4 sc = a.use_side ? load_side_chunk<8>(a, n, ch0, KVEC) : i32x4{0, 0, 0, 0};
-    epilogue_store_i8<8>(v, a, n, ch0, KVEC, sc);
-  } else {
-    epilogue_store_float<DT, 8>(v, a, n, ch0, KVEC);
-  }
+  if constexpr (DT == FCONV_INT8)
+    epilogue_store_i8<8>(v, a, n, ch0, KVEC, sc, bias, cis);
+  else
+    epilogue_store_float<DT, 8>(v, a, n, ch0, KVEC, P);
 }
 
 // ------------------------------------------------------------- dispatch
