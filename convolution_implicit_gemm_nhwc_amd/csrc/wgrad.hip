@@ -832,33 +832,45 @@ void wgrad_dma_kernel(WgArgs a) {
 }
 
 // dw[i] = sum over pixel ranges z of part[z][i], in a fixed association
-// (zeros for no range).  A workgroup owns 16 four-element columns; its 16
-// lane groups each add the ranges z = g, g + 16, g + 32, ... in increasing
-// order, and the 16 group sums are then added in group order.  Many ranges
-// are thus read in parallel (the sum is bound by the partials' bandwidth,
-// not by the latency of one long chain), and every run adds the same values
-// in the same order.
-constexpr int kRedCols = 16;    // four-element columns per workgroup
-constexpr int kRedGroups = 16;  // lane groups over the ranges
-
+// (zeros for no range).  A workgroup of 256 threads owns 256/G four-element
+// columns; its G lane groups each add the ranges z = g, g + G, g + 2G, ... in
+// increasing order, with up to four of those loads in flight together, and
+// the G group sums are then added in group order.  Many ranges are thus read
+// in parallel (the sum is bound by the partials' bandwidth, not by the
+// latency of one long chain), and every run of a plan adds the same values in
+// the same order.  G = 4 for up to 8 ranges (a quarter of the workgroups that
+// 16 groups would need, most of whose threads would have no range to read),
+// else 16.
+template <int G>
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ part,
                                                            void* __restrict__ dw, int splits,
                                                            int64_t lp, int64_t L, int out_bf16) {
-  __shared__ f32x4 red[kRedGroups][kRedCols];
-  const int col = threadIdx.x % kRedCols;
-  const int g = threadIdx.x / kRedCols;
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * kRedCols + col) * 4;
+  constexpr int COLS = 256 / G;
+  __shared__ f32x4 red[G][COLS];
+  const int col = threadIdx.x % COLS;
+  const int g = threadIdx.x / COLS;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * COLS + col) * 4;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if (i0 < L) {
-    for (int z = g; z < splits; z += kRedGroups)
-      s += *reinterpret_cast<const f32x4*>(part + z * lp + i0);
+    for (int z0 = g; z0 < splits; z0 += 4 * G) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int z = z0 + u * G;
+        v[u] = z < splits ? *reinterpret_cast<const f32x4*>(part + z * lp + i0)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u * G < splits) s += v[u];
+    }
   }
   red[g][col] = s;
   __syncthreads();
   if (g != 0 || i0 >= L) return;
   s = red[0][col];
 #pragma unroll
-  for (int q = 1; q < kRedGroups; ++q) s += red[q][col];
+  for (int q = 1; q < G; ++q) s += red[q][col];
   if (out_bf16) {
     uint16_t* o = static_cast<uint16_t*>(dw) + i0;
     if (i0 + 4 <= L && (L & 3) == 0) {
@@ -876,6 +888,22 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restri
       for (int t = 0; t < 4 && i0 + t < L; ++t) o[t] = s[t];
     }
   }
+}
+
+// The sum of the ranges (splits = 0: zeros) with the lane groups chosen by
+// the number of ranges.
+hipError_t launch_wgrad_reduce(const float* part, void* dw, int splits, int64_t lp, int64_t L,
+                               int out_bf16, hipStream_t s) {
+  if (splits <= 8) {
+    const int grid = static_cast<int>((L + 4 * 64 - 1) / (4 * 64));
+    hipLaunchKernelGGL(wgrad_reduce_kernel<4>, dim3(grid), dim3(256), 0, s, part, dw, splits, lp,
+                       L, out_bf16);
+  } else {
+    const int grid = static_cast<int>((L + 4 * 16 - 1) / (4 * 16));
+    hipLaunchKernelGGL(wgrad_reduce_kernel<16>, dim3(grid), dim3(256), 0, s, part, dw, splits,
+                       lp, L, out_bf16);
+  }
+  return hipGetLastError();
 }
 
 template <int DT, int TK, bool VEC>
@@ -1087,13 +1115,12 @@ fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan p, void* stream, const void* 
     return FCONV_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t L = p->dw_elems;
-  const int reduce_grid = static_cast<int>((L + 4 * kRedCols - 1) / (4 * kRedCols));
   const int out_bf16 = p->out_fp32 ? 0 : 1;
   if (p->M == 0) {
     // Empty batch: the gradient is zero.
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(reduce_grid), dim3(256), 0, s,
-                       static_cast<const float*>(nullptr), dw, 0, p->lp, L, out_bf16);
-    return hipGetLastError() == hipSuccess ? FCONV_OK : FCONV_ERR_DEVICE;
+    return launch_wgrad_reduce(nullptr, dw, 0, p->lp, L, out_bf16, s) == hipSuccess
+               ? FCONV_OK
+               : FCONV_ERR_DEVICE;
   }
   WgArgs a;
   a.x = x;
@@ -1119,11 +1146,9 @@ fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan p, void* stream, const void* 
   hipError_t e = p->d.dtype == FCONV_BF16 ? launch_wgrad_dt<FCONV_BF16>(p, a, s)
                                            : launch_wgrad_dt<FCONV_FP32>(p, a, s);
   if (e != hipSuccess) return FCONV_ERR_DEVICE;
-  if (p->splits > 1) {
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(reduce_grid), dim3(256), 0, s,
-                       static_cast<const float*>(workspace), dw, p->splits, p->lp, L, out_bf16);
-    if (hipGetLastError() != hipSuccess) return FCONV_ERR_DEVICE;
-  }
+  if (p->splits > 1 && launch_wgrad_reduce(static_cast<const float*>(workspace), dw, p->splits,
+                                            p->lp, L, out_bf16, s) != hipSuccess)
+    return FCONV_ERR_DEVICE;
   return FCONV_OK;
 }
 
