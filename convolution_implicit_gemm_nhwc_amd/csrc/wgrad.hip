@@ -62,13 +62,15 @@ struct fconv_wgrad_plan_s {
   int32_t ring;      // direct-to-LDS kernel: stages in its LDS ring (4 or 8)
   int32_t tk;        // output channels per tile (64, 128, or 256 with 8 waves)
   bool ksplit;       // bf16 4-stage ring, 64/128-channel tile: two wave groups split each range
+  bool halo;         // bf16 3x3 stride 1: the row-halo kernel (ranges of output rows)
+  int32_t rps;       // row-halo kernel: output rows per step (2 when Wo <= 32, else 1)
   int32_t tiles_k, tiles_kk;
   int32_t splits;    // pixel ranges
   int32_t m_per_split;
   int64_t lp;        // partial tile stride in floats (Kg*K rounded up to 4)
   size_t ws_bytes;
   int64_t x_elems, dy_elems, dw_elems;
-  fconv::FastDiv hw_div, wo_div;
+  fconv::FastDiv hw_div, wo_div, ho_div;
   const char* kernel_name;
 };
 
@@ -99,6 +101,7 @@ struct WgArgs {
   uint32_t x_bytes, dy_bytes;
   uint32_t hw_mul, hw_add, hw_shift, wo_mul, wo_add, wo_shift;
   int32_t wo_ge_e;  // Wo >= pixels per gather group: one wrap at most
+  uint32_t ho_mul, ho_add, ho_shift;  // row-halo kernel: output row / Ho
 };
 
 __device__ inline uint32_t fast_div(uint32_t n, uint32_t mul, uint32_t add, uint32_t shift) {
@@ -831,6 +834,274 @@ void wgrad_dma_kernel(WgArgs a) {
   wg_store<NI, NJ>(a, acc, split, k0, kk0, wk, wkk, lane);
 }
 
+// Row-halo weight gradient (bf16, 3x3, stride 1): the direct-to-LDS kernel
+// copies, for every 128-column tile, the patch rows of its two or three taps,
+// so each input pixel crosses from L2 into LDS once per tap tile and each
+// gradient pixel once per tile.  Here a workgroup owns 9 taps x 32 input
+// channels x 64 output channels of dw over a range of output rows, and every
+// input row and gradient row of the range is copied into LDS once: the taps
+// are LDS address offsets.
+//
+// Waves 0-3 (one per SIMD) run the MFMAs; wave m holds the 9 taps x 16
+// channels (channel tile m>>1 of the 32) x 32 output channels (tiles
+// 2(m&1), 2(m&1)+1 of the 64): 18 accumulator tiles.  Waves 4-7 issue every
+// copy: their code holds no LDS reads that a pending copy could alias, and
+// the MFMA waves' code no copies, so the compiler adds no memory-count wait to
+// either.  A step is one output row (Wo > 32: two 32-pixel blocks of the row)
+// or two output rows (Wo <= 32: one block each); per block a wave reads two
+// dy fragments and nine patch fragments (gfx950's transposed LDS read, as in
+// the direct-to-LDS kernel) and runs 18 MFMAs.
+//
+// Input rows live in a ring of twelve 64-pixel slots (32 channels, 4 KiB):
+// rows are numbered in the order the workgroup's output rows first need them
+// (row r of output row u is number k0(u) + r; k0 advances by 1 per output row
+// and by 3 at an image change), number k in slot k % 12.  The rows of the
+// three steps in flight span at most twelve numbers: 5 + 2 per image change
+// for one-row steps (at most two changes in three rows), 8 + 2 per change for
+// two-row steps (at most two changes in six rows when Ho >= 3).  Pixel place X (= input
+// column + left pad) holds its four 16-byte chunks at X*64 + 16*(c ^ 2((X>>1)&1)).
+// Gradient rows: a ring of three 8 KiB slots, one per step (64 pixel places
+// of 64 channels, the direct-to-LDS kernel's swizzle).  In the interval that
+// ends with the barrier after MFMA step t, the copy waves copy step t+2's
+// new input rows and gradient rows, then wait for step t+1's (issued one
+// interval earlier): the MFMA waves read only rows published by a barrier.
+constexpr int kWhThreads = 512;
+constexpr int kWhXSlots = 12;
+constexpr int kWhXSlot = 4096;   // 64 pixel places x 32 channels x 2 bytes
+constexpr int kWhDySlots = 3;
+constexpr int kWhDySlot = 8192;  // 64 pixel places x 64 channels x 2 bytes
+
+// Row number of row 0 of output row gr (flattened n*Ho + ho) for a workgroup
+// that starts at output row ho0 of image n0.
+__device__ inline int wh_k0(const WgArgs& a, int gr, int n0, int ho0) {
+  const int n = static_cast<int>(fast_div(static_cast<uint32_t>(gr), a.ho_mul, a.ho_add, a.ho_shift));
+  const int ho = gr - n * a.Ho;
+  if (n == n0) return ho - ho0;
+  return a.Ho + 2 - ho0 + (n - n0 - 1) * (a.Ho + 2) + ho;
+}
+
+__device__ inline int wh_xswz(int X) { return ((X >> 1) & 1) << 1; }
+
+template <int RPS>
+__global__ __launch_bounds__(kWhThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void wgrad_halo_kernel(WgArgs a) {
+  using Cfg = DmaCfg<FCONV_BF16, 64>;  // the 128-byte gradient rows' swizzle
+  __shared__ __attribute__((aligned(1024))) char xring[kWhXSlots * kWhXSlot];
+  __shared__ __attribute__((aligned(1024))) char dring[kWhDySlots * kWhDySlot];
+
+  const int nb = gridDim.x;
+  const int bidx = blockIdx.x;
+  const int logical = (nb % 8 == 0) ? (bidx % 8) * (nb / 8) + bidx / 8 : bidx;
+  if (logical >= a.blocks) return;  // uniform per workgroup
+  const int tiles = a.tiles_k * a.tiles_kk;
+  const int split = logical / tiles;
+  const int tile = logical % tiles;
+  const int kb = tile % a.tiles_k;   // 64-channel block of K
+  const int cs = tile / a.tiles_k;   // 32-channel slice of C
+  const int rows_total = a.N * a.Ho;
+  const int g0 = split * a.m_per_split;  // first output row
+  const int nrows = min(g0 + a.m_per_split, rows_total) - g0;
+  const int steps = (nrows + RPS - 1) / RPS;
+  const int n0 = static_cast<int>(fast_div(static_cast<uint32_t>(g0), a.ho_mul, a.ho_add, a.ho_shift));
+  const int ho0 = g0 - n0 * a.Ho;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (wave < 4) {
+    const int ct = wave >> 1, kp = wave & 1;
+    const int j16 = lane & 15, g = lane >> 4;
+    // Fragment offsets: gradient, inside a block (pixel place p of its
+    // first); input, inside a row slot for block bb (place 32bb + p + s for
+    // Wo > 32, else p + s; places past 63 belong to pixels past Wo, whose
+    // gradient is zero, and read place 63 instead, inside the slot).
+    int dyo[2][2], xo[2][2][3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = 8 * g + 4 * h + (j16 >> 2);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int cb = ((2 * kp + kt) * 16 + 4 * (j16 & 3)) * 2;
+        dyo[h][kt] = p * Cfg::RB_DY + (((cb >> 4) ^ dma_swz<FCONV_BF16, Cfg::RB_DY>(p)) << 4) + (cb & 15);
+      }
+      const int cbx = (ct * 16 + 4 * (j16 & 3)) * 2;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          const int X = min((RPS == 1 ? 32 * bb : 0) + p + s, 63);
+          xo[bb][h][s] = X * 64 + (((cbx >> 4) ^ wh_xswz(X)) << 4) + (cbx & 15);
+        }
+    }
+    f32x4 acc[9][2];
+#pragma unroll
+    for (int q = 0; q < 9; ++q)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[q][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    barrier();  // steps 0 and 1 have landed
+    for (int t = 0; t < steps; ++t) {
+      const char* dbase = dring + (t % kWhDySlots) * kWhDySlot;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        // Block bb: pixels 32bb.. of output row RPS*t (RPS = 1), or output
+        // row RPS*t + bb (RPS = 2); rows past the range are skipped.
+        const int u = RPS * t + (RPS == 2 ? bb : 0);
+        if (u >= nrows) continue;  // uniform
+        const int k0 = wh_k0(a, g0 + u, n0, ho0);
+        const int pix0 = RPS == 1 ? 32 * bb : 0;
+        const char* db = dbase + (RPS == 2 ? bb * 4096 : 0) + pix0 * Cfg::RB_DY;
+        v4i16 al[2][2], bl[9][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            al[kt][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(db + dyo[h][kt]));
+#pragma unroll
+          for (int r = 0; r < 3; ++r) {
+            const char* xb = xring + ((k0 + r) % kWhXSlots) * kWhXSlot;
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+              bl[3 * r + s][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t)(xb + xo[bb][h][s]));
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 af = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(al[kt][0], al[kt][1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int q = 0; q < 9; ++q) {
+            const bf16x8 bf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(bl[q][0], bl[q][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[q][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[q][kt], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this step's reads are done
+      barrier();
+    }
+    // The tile: lane holds D[k][kk] for k = 64 kb + 16 (2 kp + kt) + 4 g + 0..3
+    // and kk = (r, s, c) with c = 32 cs + 16 ct + j16.
+    const bool kvec4 = (a.K & 3) == 0;
+#pragma unroll
+    for (int q = 0; q < 9; ++q)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int k = kb * 64 + (2 * kp + kt) * 16 + 4 * g;
+        const int kk = q * a.C + cs * 32 + ct * 16 + j16;
+        const f32x4 v = acc[q][kt];
+        const int64_t base = static_cast<int64_t>(kk) * a.K + k;
+        if (a.out_mode == 0) {
+          float* o = static_cast<float*>(a.out) + split * a.lp + base;
+          if (kvec4) *reinterpret_cast<f32x4*>(o) = v;
+          else for (int t4 = 0; t4 < 4; ++t4) o[t4] = v[t4];
+        } else if (a.out_mode == 1) {
+          float* o = static_cast<float*>(a.out) + base;
+          if (kvec4) *reinterpret_cast<f32x4*>(o) = v;
+          else for (int t4 = 0; t4 < 4; ++t4) o[t4] = v[t4];
+        } else {
+          uint16_t* o = static_cast<uint16_t*>(a.out) + base;
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (uint32_t(f32_to_bf16_rne(v[1])) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (uint32_t(f32_to_bf16_rne(v[3])) << 16);
+          *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+        }
+      }
+  } else {
+    const int e = wave - 4;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.dy, a.dy_bytes);
+    // This wave copies KiB e of every input row: per lane the source offset
+    // inside the row (out-of-range columns: 2^31, which keeps the sum with any
+    // row's offset, below 2^31, out of range), and KiBs e and e + 4 of every
+    // gradient slot.
+    uint32_t xoff;
+    {
+      const int pos = e * 1024 + lane * 16;
+      const int X = pos / 64;
+      const int c = ((pos % 64) >> 4) ^ wh_xswz(X);
+      const int wi = X - a.pl;
+      xoff = static_cast<unsigned>(wi) < static_cast<unsigned>(a.W)
+                 ? static_cast<uint32_t>((wi * a.C + cs * 32 + c * 8) * 2)
+                 : kOutOfRange;
+    }
+    int dpx[2], dch[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int pos = (e + 4 * i) * 1024 + lane * 16;
+      const int p = pos / Cfg::RB_DY;  // pixel place in the 64-place slot
+      dpx[i] = p;
+      dch[i] = kb * 64 + (((pos % Cfg::RB_DY) >> 4) ^ dma_swz<FCONV_BF16, Cfg::RB_DY>(p)) * 8;
+    }
+    // Step u's new input rows and its gradient rows; returns the copies issued.
+    auto copy_step = [&](int u) -> int {
+      if (u >= steps) return 0;
+      int issued = 0;
+#pragma unroll
+      for (int b = 0; b < RPS; ++b) {
+        const int ur = RPS * u + b;
+        if (ur >= nrows) break;
+        const int gr = g0 + ur;
+        const int n = static_cast<int>(fast_div(static_cast<uint32_t>(gr), a.ho_mul, a.ho_add, a.ho_shift));
+        const int ho = gr - n * a.Ho;
+        const int k0 = wh_k0(a, gr, n0, ho0);
+        // Rows 0 and 1 of output row ur are rows 1 and 2 of the previous one
+        // unless ur starts the range or an image.
+        for (int r = (ur == 0 || ho == 0) ? 0 : 2; r < 3; ++r) {
+          const int hi = ho - a.pt + r;
+          const bool ok = static_cast<unsigned>(hi) < static_cast<unsigned>(a.H);
+          const uint32_t rbase = static_cast<uint32_t>((n * a.H + hi) * a.W * a.C * 2);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              xr, (lds_ptr_t)(xring + ((k0 + r) % kWhXSlots) * kWhXSlot + e * 1024), 16,
+              ok ? rbase + xoff : kOutOfRange, 0, 0, 0);
+          ++issued;
+        }
+      }
+      char* ds = dring + (u % kWhDySlots) * kWhDySlot;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // RPS = 1: places 0..63 of row u; RPS = 2: places 32b + wo of row 2u + b.
+        const int b = RPS == 2 ? dpx[i] >> 5 : 0;
+        const int wo = RPS == 2 ? dpx[i] & 31 : dpx[i];
+        const int ur = RPS * u + b;
+        const bool ok = ur < nrows && wo < a.Wo;
+        const uint32_t src =
+            ok ? static_cast<uint32_t>(((static_cast<int64_t>(g0 + ur) * a.Wo + wo) * a.K + dch[i]) * 2)
+               : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_ptr_t)(ds + (e + 4 * i) * 1024), 16, src,
+                                                 0, 0, 0);
+        ++issued;
+      }
+      return issued;
+    };
+    copy_step(0);
+    copy_step(1);
+    // Steps 0 and 1: the MFMA waves read only rows published by a barrier.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    barrier();
+    for (int t = 0; t < steps; ++t) {
+      const int c = copy_step(t + 2);
+      // Step t+1's copies (issued one interval earlier) have landed; this
+      // interval's may stay in flight.
+      switch (c) {
+#define FCONV_WH_WAIT(n) \
+  case n:                \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(n)); \
+    break;
+        FCONV_WH_WAIT(0) FCONV_WH_WAIT(1) FCONV_WH_WAIT(2) FCONV_WH_WAIT(3) FCONV_WH_WAIT(4)
+        FCONV_WH_WAIT(5) FCONV_WH_WAIT(6) FCONV_WH_WAIT(7) FCONV_WH_WAIT(8)
+#undef FCONV_WH_WAIT
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+      }
+      barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
+
 // dw[i] = sum over pixel ranges z of part[z][i], in a fixed association
 // (zeros for no range).  A workgroup of 256 threads owns 256/G four-element
 // columns; its G lane groups each add the ranges z = g, g + G, g + 2G, ... in
@@ -923,6 +1194,16 @@ hipError_t launch_wgrad_dma(const WgArgs& a, hipStream_t s) {
 
 template <int DT>
 hipError_t launch_wgrad_dt(const fconv_wgrad_plan_s* p, const WgArgs& a, hipStream_t s) {
+  if constexpr (DT == FCONV_BF16) {
+    if (p->halo) {
+      const int grid = (a.blocks + 7) / 8 * 8;
+      if (p->rps == 2)
+        hipLaunchKernelGGL(wgrad_halo_kernel<2>, dim3(grid), dim3(kWhThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL(wgrad_halo_kernel<1>, dim3(grid), dim3(kWhThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (p->dma && p->tk == 256) return launch_wgrad_dma<DT, 256, 4>(a, s);
   if constexpr (DT == FCONV_BF16) {
     if (p->dma && p->ksplit)
@@ -945,7 +1226,9 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
-const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring, bool ksplit) {
+const char* wgrad_kernel_name(int dtype, int tk, bool vec, bool dma, int ring, bool ksplit,
+                              bool halo) {
+  if (halo) return "wgrad_halo_bf16";
   if (dma && tk == 256) return "wgrad_dma_bf16_256";
   if (dma && ksplit) return tk == 128 ? "wgrad_dma2_bf16_128" : "wgrad_dma2_bf16_64";
   if (dma && ring == 8) {
@@ -1062,7 +1345,42 @@ fconv_status fconv_wgrad_plan_create(const fconv_desc* desc, fconv_wgrad_plan* o
   p->ws_bytes = splits > 1 ? static_cast<size_t>(splits * p->lp * 4) : 0;
   p->hw_div = make_fast_div(static_cast<uint32_t>(p->Ho * p->Wo));
   p->wo_div = make_fast_div(static_cast<uint32_t>(p->Wo));
-  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring, p->ksplit);
+  // bf16, 3x3, stride 1, 32-channel input slices and 64-channel output
+  // blocks, padded input rows of 33 to 64 pixels: the row-halo kernel, which
+  // copies every input and gradient row of its range once.  Ranges of whole
+  // output rows, about one workgroup per CU.  Rows of at most 32 pixels (two
+  // rows per step, Ho >= 3) only when FCONV_WGRAD_KERNEL=halo pins it: 40.3
+  // against 31.0 us for the direct-to-LDS kernel on the 28x28x256 layer, where
+  // the 56x56x64 layer takes 22.0 against 25.5-25.9.  FCONV_WGRAD_KERNEL=dma
+  // or staged pins the other kernels.
+  const bool pin_halo = force && strcmp(force, "halo") == 0;
+  p->halo = p->dma && d.dtype == FCONV_BF16 && d.R == 3 && d.S == 3 && d.stride_h == 1 &&
+            d.stride_w == 1 && d.C % 32 == 0 && d.K % 64 == 0 && d.W + p->pl + p->pr <= 64 &&
+            (p->Wo > 32 || (pin_halo && p->Ho >= 3)) && !(force && strcmp(force, "dma") == 0);
+  if (p->halo) {
+    p->rps = p->Wo > 32 ? 1 : 2;
+    p->tiles_k = d.K / 64;
+    p->tiles_kk = d.C / 32;
+    const int64_t tl = static_cast<int64_t>(p->tiles_k) * p->tiles_kk;
+    const int64_t rows = static_cast<int64_t>(d.N) * p->Ho;
+    int64_t sp = kWgTargetBlocks / 2 / tl;
+    if (sp > rows) sp = rows;
+    if (sp < 1) sp = 1;
+    const int64_t rps_split = rows > 0 ? (rows + sp - 1) / sp : 1;  // output rows per range
+    sp = rows > 0 ? (rows + rps_split - 1) / rps_split : 1;
+    if (sp * tl >= INT32_MAX) {
+      delete p;
+      return FCONV_ERR_UNSUPPORTED;
+    }
+    p->splits = static_cast<int32_t>(sp);
+    p->m_per_split = static_cast<int32_t>(rps_split);
+    p->ws_bytes = sp > 1 ? static_cast<size_t>(sp * p->lp * 4) : 0;
+    p->ring = 0;
+    p->tk = 64;
+    p->ksplit = false;
+  }
+  p->ho_div = make_fast_div(static_cast<uint32_t>(p->Ho));
+  p->kernel_name = wgrad_kernel_name(d.dtype, p->tk, p->vec, p->dma, p->ring, p->ksplit, p->halo);
   // FCONV_LOG=1 (environment): the plan's decisions on stderr.
   const char* lg = getenv("FCONV_LOG");
   if (lg && *lg && strcmp(lg, "0") != 0)
@@ -1143,6 +1461,7 @@ fconv_status fconv_wgrad_plan_run(fconv_wgrad_plan p, void* stream, const void* 
   a.hw_mul = p->hw_div.mul; a.hw_add = p->hw_div.add; a.hw_shift = p->hw_div.shift;
   a.wo_mul = p->wo_div.mul; a.wo_add = p->wo_div.add; a.wo_shift = p->wo_div.shift;
   a.wo_ge_e = p->Wo >= p->E;
+  a.ho_mul = p->ho_div.mul; a.ho_add = p->ho_div.add; a.ho_shift = p->ho_div.shift;
   hipError_t e = p->d.dtype == FCONV_BF16 ? launch_wgrad_dt<FCONV_BF16>(p, a, s)
                                            : launch_wgrad_dt<FCONV_FP32>(p, a, s);
   if (e != hipSuccess) return FCONV_ERR_DEVICE;

@@ -55,13 +55,30 @@ CASES = [
     (4, 20, 20, 64, 64, 3, 3, 1, "SAME"),
     (1, 1, 1, 8, 8, 1, 1, 1, "VALID"),
     (2, 12, 12, 128, 256, 3, 3, 2, "SAME"),
+    # bf16 3x3 stride 1 shapes of the row-halo kernel: one-row steps with two
+    # 32-pixel blocks (Wo > 32, the widest 62), two-row steps (Wo <= 32),
+    # VALID, three input slices and output blocks, and images of 1 and 3
+    # output rows (every step or every other one crosses an image).
+    (3, 9, 40, 32, 64, 3, 3, 1, "SAME"),
+    (2, 5, 62, 32, 64, 3, 3, 1, "SAME"),
+    (5, 7, 30, 64, 128, 3, 3, 1, "SAME"),
+    (3, 12, 20, 96, 192, 3, 3, 1, "VALID"),
+    (7, 3, 10, 32, 64, 3, 3, 1, "SAME"),
+    (9, 1, 40, 32, 64, 3, 3, 1, "SAME"),
 ]
 
 
 def _pin(kernel, monkeypatch):
-    if kernel == "staged":
-        monkeypatch.setenv("FCONV_WGRAD_KERNEL", "staged")
-    elif kernel in ("ring4", "ring8"):
+    """'default': the plan's own choice (the row-halo kernel where it applies);
+    'halo' pins the row-halo kernel also on rows of at most 32 pixels; the
+    others pin the direct-to-LDS kernel's variants or the staged one."""
+    if kernel in ("staged", "halo"):
+        monkeypatch.setenv("FCONV_WGRAD_KERNEL", kernel)
+        return
+    if kernel == "default":
+        return
+    monkeypatch.setenv("FCONV_WGRAD_KERNEL", "dma")
+    if kernel in ("ring4", "ring8"):
         monkeypatch.setenv("FCONV_WGRAD_RING", kernel[-1])
     elif kernel == "tk256":
         monkeypatch.setenv("FCONV_WGRAD_TK", "256")
@@ -69,12 +86,17 @@ def _pin(kernel, monkeypatch):
         monkeypatch.setenv("FCONV_WGRAD_GROUPS", "1")
 
 
-@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk256", "groups1", "staged"])
+@pytest.mark.parametrize("kernel", ["default", "halo", "ring4", "ring8", "tk256", "groups1",
+                                    "staged"])
 @pytest.mark.parametrize("out_fp32", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", CASES)
 def test_wgrad_small_shapes(case, dtype, out_fp32, kernel, monkeypatch):
-    """Every kernel: the direct-to-LDS one (where C and K fill 16-byte chunks)
+    """Every kernel: the plan's own choice (bf16 3x3 stride 1 with 32-channel
+    input slices, 64-channel output blocks and rows of 33-64 pixels: the
+    row-halo kernel), the row-halo kernel pinned (two-row steps on narrower
+    rows), the
+    direct-to-LDS one (where C and K fill 16-byte chunks)
     with its 4- and 8-stage rings (FCONV_WGRAD_RING; the default is 4 for
     bf16, 8 for fp32), bf16 with K > 128 on 256- instead of 128-channel tiles
     (FCONV_WGRAD_TK=256), bf16 64/128-channel tiles with one wave group
@@ -129,7 +151,8 @@ def test_wgrad_is_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("kernel", ["ring4", "ring8", "tk256", "groups1", "staged"])
+@pytest.mark.parametrize("kernel", ["default", "halo", "ring4", "ring8", "tk256", "groups1",
+                                    "staged"])
 @pytest.mark.parametrize("name", list(wl.WGRAD_LAYERS))
 def test_wgrad_full_workload(name, kernel, monkeypatch):
     """The full benchmark workloads, every element against the oracle."""

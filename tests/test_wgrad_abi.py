@@ -80,8 +80,9 @@ def test_workloads_and_workspace():
         kg_k = L.R * L.S * L.C * L.K
         # partial sums: a whole number of fp32 dW copies (or none)
         assert g.workspace_bytes % (4 * ((kg_k + 3) // 4)) == 0
-        assert g.kernel_name.startswith(("wgrad_dma_bf16", "wgrad_dma2_bf16") if L.dtype == "bf16"
-                                        else "wgrad_dma8_f32")
+        want = {"wgrad_3x3_64_bf16": "wgrad_halo_bf16", "wgrad_3x3_bf16": "wgrad_dma2_bf16_128",
+                "wgrad_3x3_fp32": "wgrad_dma8_f32_128"}
+        assert g.kernel_name == want[L.name], (L.name, g.kernel_name)
 
 
 def test_run_checks_arguments():
@@ -130,8 +131,25 @@ def test_staged_kernel_can_be_pinned(monkeypatch):
     g = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g.kernel_name == "wgrad_bf16_128"
     monkeypatch.delenv("FCONV_WGRAD_KERNEL")
+    gh = fc.WgradPlan(32, 56, 56, 64, 64, 3, 3, 1, "SAME", "bf16")
+    assert gh.kernel_name == "wgrad_halo_bf16"
+    # 2 input slices x 1 output block, 128 ranges of 14 output rows: one
+    # workgroup per CU, 128 fp32 dW copies in the workspace
+    assert gh.workspace_bytes == 128 * 9 * 64 * 64 * 4
+    assert fc.WgradPlan(32, 56, 56, 64, 64, 3, 3, 2, "SAME", "bf16").kernel_name != \
+        "wgrad_halo_bf16"  # stride 2
+    assert fc.WgradPlan(32, 56, 56, 48, 64, 3, 3, 1, "SAME", "bf16").kernel_name != \
+        "wgrad_halo_bf16"  # C not a multiple of 32
+    assert fc.WgradPlan(4, 8, 70, 32, 64, 3, 3, 1, "SAME", "bf16").kernel_name != \
+        "wgrad_halo_bf16"  # padded rows wider than 64 pixels
     g2 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
-    assert g2.kernel_name == "wgrad_dma2_bf16_128"
+    assert g2.kernel_name == "wgrad_dma2_bf16_128"  # rows of 28 pixels
+    monkeypatch.setenv("FCONV_WGRAD_KERNEL", "halo")
+    assert fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16").kernel_name == \
+        "wgrad_halo_bf16"
+    monkeypatch.setenv("FCONV_WGRAD_KERNEL", "dma")
+    assert fc.WgradPlan(32, 56, 56, 64, 64, 3, 3, 1, "SAME", "bf16").kernel_name == \
+        "wgrad_dma2_bf16_64"
     monkeypatch.setenv("FCONV_WGRAD_TK", "256")
     g256 = fc.WgradPlan(16, 28, 28, 256, 256, 3, 3, 1, "SAME", "bf16")
     assert g256.kernel_name == "wgrad_dma_bf16_256"
