@@ -1069,6 +1069,271 @@ void conv_tile_kernel(ConvArgs a) {
   }
 }
 
+// The tiled kernel with a copy role (int8 and bf16, 128- and 64-pixel tiles):
+// 12 waves.  Waves 0-3, one per SIMD and started first, issue every
+// buffer->LDS copy of a stage, BM/32 of pixel rows and 4 of filter rows each,
+// three stages ahead, and the epilogue values' copies before stage 0.  Waves
+// 4-11, two per SIMD, only read fragments and run MFMAs, as the 2 x 4 grid of
+// the 8-wave kernel (BM/2 pixels x 32 channels each): no memory instruction,
+// no copy arithmetic and no memory-count wait in their loop.  Step st reads
+// stage st + 1's fragments while stage st's MFMAs run; before the barrier
+// that ends it, the copy waves have issued stage st + 3 into the buffer of
+// stage st - 1 and waited until only those copies are in flight (stage st + 2
+// has landed), and the MFMA waves have waited for their reads.  The tile,
+// stage layout, slot swizzle and epilogue are the 8-wave kernel's.  Measured
+// (same box, graph replay): 26.2-26.3 -> 23.4-23.6 us on the 3x3 256-channel
+// bf16 layer, 22.1 -> 20.3 (5x5 CBNA) and 22.4-22.6 -> 20.7-20.8 (7x7 stride-2
+// CBNA, 64-pixel tiles), 19.3 -> 19.0 on the strided int8 layer pinned to
+// 128-pixel tiles, same outputs bit for bit; fp32 153.3 against 154.3, so
+// fp32 keeps the 8-wave kernel.
+constexpr int kCwThreads = 768;
+
+template <int DT, bool KVEC, int BM>
+__global__ __launch_bounds__(kCwThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void conv_tile_cw_kernel(ConvArgs a) {
+  static_assert(BM == 128 || BM == 64, "pixel rows per tile");
+  constexpr int PI = BM / 32;  // 16-pixel MFMA tiles per MFMA wave
+  constexpr int PC = BM / 32;  // pixel copies per copy wave per stage
+  constexpr int CPW = PC + 4;  // copies per copy wave per stage
+  constexpr int TB = (BM + kTileBN) * kTileStage;
+  using Acc = typename Dt<DT>::Acc;
+  constexpr int E = Dt<DT>::kChunk;
+  constexpr int ES = 16 / E;
+  constexpr int SE = kTileStage / ES;
+  __shared__ __attribute__((aligned(1024))) char buf0[TB];
+  __shared__ __attribute__((aligned(1024))) char buf1[TB];
+  __shared__ __attribute__((aligned(1024))) char buf2[TB];
+  __shared__ __attribute__((aligned(1024))) char buf3[TB];
+  __shared__ __attribute__((aligned(1024))) char epar[DT == FCONV_INT8 ? 2048 + BM * 128 : 5 * 1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  const int nst = a.R * a.S * (a.C / SE);
+
+  if (wave < 4) {
+    const int e = wave;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wp_bytes);
+    // Copy h of this wave: rows 8 (e + 4h) .. +7 of the pixel block and of
+    // the filter block; lane l fills slot l & 7 of row 8 (e + 4h) + (l >> 3).
+    const int q = (lane & 7) ^ ((lane >> 3) & 7);
+    int hb[PC], wb[PC], pbase[PC];
+    uint32_t wbase[4];
+    const int RS = a.wrow_bytes;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int row = 8 * (e + 4 * h) + (lane >> 3);
+      wbase[h] = static_cast<uint32_t>((blockIdx.y * kTileBN + row) * RS + q * 16);
+    }
+#pragma unroll
+    for (int h = 0; h < PC; ++h) {
+      const int row = 8 * (e + 4 * h) + (lane >> 3);
+      const int m = blockIdx.x * BM + row;
+      const int mm = m < a.M ? m : 0;
+      const uint32_t qq = fast_div(static_cast<uint32_t>(mm), a.wo_mul, a.wo_add, a.wo_shift);
+      const int wo = mm - static_cast<int>(qq) * a.Wo;
+      const uint32_t n = fast_div(qq, a.ho_mul, a.ho_add, a.ho_shift);
+      const int ho = static_cast<int>(qq) - static_cast<int>(n) * a.Ho;
+      hb[h] = m < a.M ? ho * a.sh - a.pt : -(1 << 20);
+      wb[h] = wo * a.sw - a.pl;
+      pbase[h] = static_cast<int>(n) * a.H * a.W * a.C * ES + q * 16;
+    }
+    // Epilogue values before the stage copies, so that the wait for stage 0
+    // covers them.
+    if constexpr (DT == FCONV_INT8) {
+      const int cbase = blockIdx.y * kTileBN;
+      if (e < 2) {
+        const float* src = e == 0 ? a.bias : a.cis_vec;
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(src, src ? static_cast<uint32_t>(a.K) * 4u : 0u);
+        const uint32_t off = lane < 32 ? static_cast<uint32_t>((cbase + 4 * lane) * 4) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)(epar + e * 1024), 16, off, 0, 0, 0);
+      }
+      if (a.use_side) {
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.side, a.side_bytes);
+#pragma unroll
+        for (int h = 0; h < PC; ++h) {
+          const int piece = e + 4 * h;  // pixels 8 piece .. +7
+          const int m = blockIdx.x * BM + 8 * piece + (lane >> 3);
+          const int c = cbase + 16 * (lane & 7);
+          const uint32_t off = m < a.M && c < a.K ? static_cast<uint32_t>(m * a.K + c) : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(epar + 2048 + piece * 1024), 16, off, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = e; v < 5; v += 4) {
+        const float* src = v == 0 ? a.bias : v == 1 ? a.bn_gamma : v == 2 ? a.bn_var : v == 3 ? a.bn_mean : a.bn_beta;
+        const bool use = v == 0 ? a.use_bias != 0 : a.use_bn != 0;
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(use ? src : nullptr, use ? static_cast<uint32_t>(a.K) * 4u : 0u);
+        const uint32_t off = lane < 32 ? static_cast<uint32_t>((blockIdx.y * kTileBN + 4 * lane) * 4) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_ptr_t)(epar + v * 1024), 16, off, 0, 0, 0);
+      }
+    }
+    const int CB = a.C * ES;
+    int nx_st = 0, nx_c0b = 0, nx_r = 0, nx_s = 0;
+    auto issue = [&](char* buf) {
+      const int st = nx_st, c0b = nx_c0b, r = nx_r, s = nx_s;
+      ++nx_st;
+      nx_c0b += kTileStage;
+      if (nx_c0b == CB) {
+        nx_c0b = 0;
+        if (++nx_s == a.S) {
+          nx_s = 0;
+          ++nx_r;
+        }
+      }
+      const bool live = st < nst;
+#pragma unroll
+      for (int h = 0; h < PC; ++h) {
+        const int hi = hb[h] + r, wi = wb[h] + s;
+        const bool ok = live && static_cast<unsigned>(hi) < static_cast<unsigned>(a.H) &&
+                        static_cast<unsigned>(wi) < static_cast<unsigned>(a.W);
+        const uint32_t off = ok ? static_cast<uint32_t>(pbase[h] + (hi * a.W + wi) * a.C * ES + c0b) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + 8 * (e + 4 * h) * kTileStage), 16, off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(buf + (BM + 8 * (e + 4 * h)) * kTileStage), 16,
+                                                 live ? wbase[h] + st * kTileStage : kOutOfRange, 0, 0, 0);
+    };
+    issue(buf0);
+    issue(buf1);
+    issue(buf2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW));  // stages 0 and 1 (and the epilogue values) have landed
+    barrier();
+    // Step st: copy stage st + 3 into the buffer of stage st - 1, then wait
+    // until only those 8 copies are in flight: stage st + 2 has landed
+    // before the barrier that ends step st.
+    int st = 0;
+    for (; st + 4 <= nst; st += 4) {
+      issue(buf3); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier();
+      issue(buf0); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier();
+      issue(buf1); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier();
+      issue(buf2); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier();
+    }
+    if (st < nst) { issue(buf3); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier(); }
+    if (st + 1 < nst) { issue(buf0); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier(); }
+    if (st + 2 < nst) { issue(buf1); __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW)); barrier(); }
+    __builtin_amdgcn_s_waitcnt(0);  // copies past the last stage (zeros) land before exit
+    return;
+  }
+
+  const int w = wave - 4;
+  const int wm = w & 1, wn = w >> 1;  // pixel half, 32-channel quarter
+  const int g = lane >> 4, col = lane & 15;
+  const int ch0 = blockIdx.y * kTileBN + (wn >> 1) * 64 + 16 * g + 8 * (wn & 1);
+  Acc acc[PI][2];
+#pragma unroll
+  for (int i = 0; i < PI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  struct Frags {
+    i32x4 pf[2][PI], ff[2][2];
+  };
+  auto read_frags = [&](const char* buf, Frags& f) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t slot = static_cast<uint32_t>(((kk * 4 + g) ^ (col & 7)) * 16);
+      const char* pl = buf + (wm * (BM / 2) + col) * kTileStage + slot;
+      const char* fb = buf + (BM + wn * 32 + col) * kTileStage + slot;
+#pragma unroll
+      for (int i = 0; i < PI; ++i) f.pf[kk][i] = *reinterpret_cast<const i32x4*>(pl + i * 16 * kTileStage);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.ff[kk][j] = *reinterpret_cast<const i32x4*>(fb + j * 16 * kTileStage);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < PI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mma_chunk(f.ff[kk][j], f.pf[kk][i], acc[i][j], static_cast<Dt<DT>*>(nullptr));
+  };
+  // Step st: read stage st + 1's fragments, run stage st's MFMAs, then wait
+  // for the reads (the buffer is recopied two steps later) and meet the copy
+  // waves at the barrier.
+  auto step = [&](const char* next, const Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+    read_frags(next, nxt);
+    mma(cur);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (PI + 2), 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * PI, 0);        // MFMA
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    barrier();
+  };
+  Frags fa, fb;
+  barrier();  // stages 0 and 1 have landed
+  read_frags(buf0, fa);
+  int st = 0;
+  for (; st + 4 <= nst; st += 4) {
+    step(buf1, fa, fb);
+    step(buf2, fb, fa);
+    step(buf3, fa, fb);
+    step(buf0, fb, fa);
+  }
+  if (st < nst) step(buf1, fa, fb);
+  if (st + 1 < nst) step(buf2, fb, fa);
+  if (st + 2 < nst) step(buf3, fa, fb);
+
+  if (ch0 >= a.K) return;
+  if constexpr (DT == FCONV_INT8) {
+    const int cl = ch0 - blockIdx.y * kTileBN;
+    const float* eb = reinterpret_cast<const float*>(epar);
+    float bias_l[8], cis_l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bias_l[e] = eb[cl + e];
+      cis_l[e] = a.cis_vec ? eb[256 + cl + e] : a.cis;
+    }
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      const int p = wm * (BM / 2) + i * 16 + col;
+      const int m = blockIdx.x * BM + p;
+      if (m >= a.M) continue;
+      int32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      i32x4 sd = i32x4{0, 0, 0, 0};
+      if (a.use_side) {
+        const i32x2 w2 = *reinterpret_cast<const i32x2*>(epar + 2048 + p * 128 + cl);
+        sd = i32x4{w2.x, w2.y, 0, 0};
+      }
+      epilogue_store_i8<8>(v, a, m, ch0, KVEC, sd, bias_l, cis_l);
+    }
+  } else {
+    FloatEpiParams<8> fpar;
+    const float* ep = reinterpret_cast<const float*>(epar) + (ch0 - blockIdx.y * kTileBN);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      fpar.bias[e] = a.use_bias ? ep[e] : 0.0f;
+      fpar.sc[e] = a.use_bn ? ep[256 + e] / __builtin_sqrtf(ep[512 + e] + a.bn_eps) : 0.0f;
+      fpar.mean[e] = a.use_bn ? ep[768 + e] : 0.0f;
+      fpar.beta[e] = a.use_bn ? ep[1024 + e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < PI; ++i) {
+      const int m = blockIdx.x * BM + wm * (BM / 2) + i * 16 + col;
+      if (m >= a.M) continue;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * j + e] = acc[i][j][e];
+      epilogue_store_float<DT, 8>(v, a, m, ch0, KVEC, fpar);
+    }
+  }
+}
+
 // Tall variant of the tiled kernel, for grids whose 128-pixel tiles would
 // need a second round over the CUs while 256-pixel ones fit in one (the
 // strided 56x56x128 layer: 392 tiles against 196).  Tile 256 pixels x 128
@@ -2891,6 +3156,19 @@ hipError_t launch_tile(const fconv_plan_s* p, const ConvArgs& a, hipStream_t s) 
   const int64_t tall_tiles = (p->M + kTall - 1) / kTall * grid.y;
   const bool tall = p->pixel_tiles == 4 || (p->pixel_tiles == 0 && tiles > cus && tall_tiles <= cus);
   const bool bm64 = p->pixel_tiles == 1 || (p->pixel_tiles == 0 && tiles * 2 <= cus);
+  // 64- and 128-pixel tiles of int8 and bf16: copy waves beside the MFMA
+  // waves, unless FCONV_TILE_ROLES=0.
+  if constexpr (DT != FCONV_FP32) {
+    if (p->tile_roles && !tall) {
+      if (bm64) {
+        const dim3 grid64(static_cast<unsigned>((p->M + 63) / 64), grid.y);
+        hipLaunchKernelGGL((conv_tile_cw_kernel<DT, true, 64>), grid64, dim3(kCwThreads), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((conv_tile_cw_kernel<DT, true, 128>), grid, dim3(kCwThreads), 0, s, a);
+      }
+      return hipGetLastError();
+    }
+  }
   if (tall) {
     const dim3 grid256(static_cast<unsigned>((p->M + kTall - 1) / kTall), grid.y);
     hipLaunchKernelGGL((conv_tile256_kernel<DT, true>), grid256, dim3(kTileThreads), 0, s, a);

@@ -108,13 +108,16 @@ constexpr int64_t kRfMaxLds = 80 * 1024;
 // FCONV_RF_PT=1|2|4 overrides the pixel tiles, FCONV_HALO_ROWS the output rows
 // per workgroup of the row-halo kernel, FCONV_TILE_BM=64|128|256 the pixel
 // rows of the tiled kernel's tile (otherwise chosen at launch from the grid
-// size).
+// size), FCONV_TILE_ROLES=0 the 8-wave tiled kernel in place of the one with
+// copy waves (int8 and bf16; fp32 always runs the 8-wave kernel).
 void choose_variant(fconv_plan_s* p) {
   const fconv_desc& d = p->d;
   p->variant = kGeneral;
   p->pixel_tiles = 1;
   p->ring_depth = 0;
   p->halo_rows = 0;
+  const char* roles = getenv("FCONV_TILE_ROLES");
+  p->tile_roles = d.dtype != FCONV_FP32 && !(roles && atoi(roles) == 0);
   const char* force0 = getenv("FCONV_FORCE_VARIANT");
   if (gemm_shape(p) && (!force0 || strcmp(force0, "gemm") == 0)) {
     p->variant = kGemm;
@@ -274,11 +277,11 @@ void log_plan(const fconv_plan_s* p, bool from_cache) {
   fprintf(stderr,
           "fconv: plan N=%d H=%d W=%d C=%d K=%d R=%d S=%d stride=%dx%d %s %s -> Ho=%d Wo=%d "
           "pads(t,b,l,r)=%d,%d,%d,%d kernel=%s%s pixel_tiles=%d ring_depth=%d halo_rows=%d "
-          "gemm_splits=%d workspace=%zu B\n",
+          "tile_roles=%d gemm_splits=%d workspace=%zu B\n",
           d.N, d.H, d.W, d.C, d.K, d.R, d.S, d.stride_h, d.stride_w,
           d.padding == FCONV_PAD_SAME ? "SAME" : "VALID", dt[d.dtype], p->Ho, p->Wo, p->pt, p->pb,
           p->pl, p->pr, p->kernel_name, from_cache ? " (autotuned)" : "", p->pixel_tiles,
-          p->ring_depth, p->halo_rows, p->gemm_splits, p->ws_bytes);
+          p->ring_depth, p->halo_rows, p->tile_roles ? 1 : 0, p->gemm_splits, p->ws_bytes);
 }
 
 }  // namespace

@@ -62,6 +62,7 @@ struct fconv_plan_s {
                         // kTiled: 64-pixel rows of the tile (1, 2, 4; 0 = by grid size)
   int32_t ring_depth;   // kResidentFilter: k-steps of patch loads in flight
   int32_t halo_rows;    // kHalo: output rows per workgroup, 0 = sized to the device
+  bool tile_roles;      // kTiled, int8/bf16, 64- or 128-pixel tiles: copy waves beside MFMA waves
   int32_t wrow_bytes;   // packed filter row stride: KgP * esize + 16 (zero pad)
   fconv::FastDiv wo_div, ho_div;
   size_t pack_bytes;    // packed filter: Kp * wrow_bytes

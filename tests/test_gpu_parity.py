@@ -427,23 +427,52 @@ def test_full_size_valid(C, K, R, variant, dtype, monkeypatch):
 
 
 
+@pytest.mark.parametrize("roles", ["1", "0"])
 @pytest.mark.parametrize("bm", [64, 128, 256])
 @pytest.mark.parametrize("K", [64, 256])
 @pytest.mark.parametrize("dtype,C,R,stages", [
     ("int8", 128, 1, 1), ("int8", 256, 1, 2), ("fp32", 96, 1, 3), ("int8", 128, 2, 4),
     ("fp32", 160, 1, 5), ("bf16", 384, 1, 6), ("fp32", 224, 1, 7), ("bf16", 64, 3, 9),
-    ("fp32", 384, 1, 12)])
-def test_tile_stage_counts(dtype, C, R, stages, K, bm, monkeypatch):
-    """The tiled kernel's loop tails: every stage count from 1 to 9 and 12,
+    ("fp32", 384, 1, 12), ("bf16", 192, 1, 3), ("int8", 640, 1, 5), ("bf16", 448, 1, 7)])
+def test_tile_stage_counts(dtype, C, R, stages, K, bm, roles, monkeypatch):
+    """The tiled kernels' loop tails: every stage count from 1 to 9 and 12,
     modulo the 4-buffer ring of the 64- and 128-pixel tiles (one 128-channel
-    tile, K = 64: two stages per barrier; two, K = 256: one per barrier) and
-    modulo the 6-stage loop trip of the 256-pixel tile's 3-buffer ring."""
+    tile, K = 64: two stages per barrier; two, K = 256: one per barrier; the
+    int8 and bf16 kernel with copy waves, FCONV_TILE_ROLES=1, one per barrier)
+    and modulo the 6-stage loop trip of the 256-pixel tile's 3-buffer ring."""
     esize = {"int8": 1, "bf16": 2, "fp32": 4}[dtype]
     assert R * R * C * esize // 128 == stages
+    if dtype == "fp32" and roles == "0":
+        pytest.skip("fp32 always runs the 8-wave tiled kernel")
     monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
     monkeypatch.setenv("FCONV_TILE_BM", str(bm))
+    monkeypatch.setenv("FCONV_TILE_ROLES", roles)
     name = check_case(tile_case(C, K, 7, 9, R, 1, "SAME", dtype), dtype)
     assert name.startswith("conv_tile_"), name
+
+
+@pytest.mark.parametrize("name,bm", [("resnet_3x3_bf16_bn", None), ("cbna_5x5_bf16", None),
+                                     ("cbna_7x7s2_bf16", None), ("resnet_3x3s2_int8", "128"),
+                                     ("resnet_3x3s2_int8", "64")])
+def test_tile_roles_bit_identical(name, bm, monkeypatch):
+    """The tiled kernel with copy waves and the 8-wave one (FCONV_TILE_ROLES=0)
+    add the same products in the same order: the same output bits on the full
+    layers (the strided int8 layer with the tiled kernel pinned)."""
+    L = wl.LAYERS[name]
+    if bm:
+        monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
+        monkeypatch.setenv("FCONV_TILE_BM", bm)
+    outs = []
+    for roles in ("1", "0"):
+        monkeypatch.setenv("FCONV_TILE_ROLES", roles)
+        inp, plan = _layer_case(L)
+        assert plan.kernel_name.startswith("conv_tile_"), plan.kernel_name
+        say("layer %s roles=%s kernel=%s" % (name, roles, plan.kernel_name))
+        y, guards = run_gpu(plan, L.dtype, inp.x, inp.w, inp.bias, inp.side, L.conv_input_scale,
+                            L.side_input_scale, inp.bn, guard=256)
+        assert guards
+        outs.append(y)
+    assert np.array_equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("C,K,H,W,R,stride,pad", [
