@@ -114,10 +114,9 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  // Hardware round to nearest even (v_cvt_pk_bf16_f32), NaN kept quiet:
+  // identical on all 2^32 inputs to the integer form of the same rounding.
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // One 16-byte fragment pair through the matrix core: 8 bf16 per lane (one

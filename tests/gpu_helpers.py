@@ -51,8 +51,9 @@ def make_plan(N, H, W, C, K, R, S, stride, padding, dtype, ops, cudnn7_order=Fal
 
 
 def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
-            prepacked_ws=None, guard=0, dev=None, activ=(0.0, 0.0)):
-    """Run the plan on device copies of numpy inputs; returns (y, guards_ok)."""
+            prepacked_ws=None, guard=0, dev=None, activ=(0.0, 0.0), raw_bits=False):
+    """Run the plan on device copies of numpy inputs; returns (y, guards_ok)
+    (y as bf16 bit patterns, uint16, for a bf16 plan with raw_bits)."""
     dev = dev or device()
     tdt = {"int8": torch.int8, "bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
     esize = {"int8": 1, "bf16": 2, "fp32": 4}[dtype]
@@ -78,7 +79,10 @@ def run_gpu(plan, dtype, x, w, bias=None, side=None, cis=1.0, sis=0.0, bn=None,
              side_input_scale=float(sis), bn=bnd, prepacked=prepacked_ws is not None,
              activ_alpha=float(activ[0]), activ_beta=float(activ[1]))
     torch.cuda.synchronize()
-    out = from_dev(y, dtype)
+    if raw_bits and dtype == "bf16":
+        out = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        out = from_dev(y, dtype)
     guards_ok = True
     if g:
         rb = raw.cpu().numpy()
