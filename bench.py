@@ -9,13 +9,17 @@ synthetic batch, inputs already resident in HBM, filter packed once per plan
 (as inference with fixed weights does).  W untimed steps, then exactly K
 timed steps bracketed by torch.cuda.synchronize(); prints ONE JSON line.
 
-The K timed steps are K fconv_plan_run calls captured into one HIP graph and
-replayed once (the graph removes the per-call host launch cost; every step
-still runs the full kernel).  The same K steps issued eagerly, one
-fconv_plan_run call each, are reported beside it, and so is a cold run with
-the 256 MB last-level cache flushed (1 GiB written) before each step.
+The K timed steps are issued one of two ways, chosen by K alone: for K >= 64,
+K fconv_plan_run calls captured into one HIP graph and replayed once (the
+graph removes the per-call host launch cost, but its submission costs a fixed
+15-20 us that only many launches amortize); for smaller K, the K calls issued
+eagerly, one launch each (the first kernel starts at once and the host's
+later launches overlap the kernels before them).  Every step runs the full
+kernel either way, and both ways are measured and reported; the other way's
+figures sit beside the headline ("graph", "eager"), and so does a cold run
+with the 256 MB last-level cache flushed (1 GiB written) before each step.
 
-value  = 2*N*Ho*Wo*K*R*S*C * K_steps / wall seconds of the graph replay, TOPS.
+value  = 2*N*Ho*Wo*K*R*S*C * K_steps / wall seconds of the K timed steps, TOPS.
 roofline: the conv kernel's algorithmic bytes (x + filter + side + y + bias,
 each once) or operations per launch / its average launch duration from HIP
 events recorded on the launch stream around the timed region.
@@ -49,10 +53,20 @@ def _code_only(text: str) -> str:
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
-LAUNCH_NOTE = ("hip graph of the K steps, replayed once (value, ms_per_step: host wall clock "
-               "with a synchronize on both sides; graph_event_us_per_step: HIP events around "
-               "that replay); roofline.kernel_avg_us: HIP events around a later replay of the "
-               "same graph queued behind others, i.e. the launches' own GPU time back to back")
+# Steps from which the timed K steps run as one HIP graph replay (below: eager
+# launches).  Measured on one MI355X (wall us per step, graph / eager): the
+# int8 3x3 layer 11.05 / 10.31 at K = 20 and 8.55 / 8.89 at K = 200; the bf16
+# 3x3 layer 25.0 / 24.15 and 22.57 / 24.26.
+GRAPH_MIN_STEPS = 64
+
+
+def launch_note(use_graph: bool) -> str:
+    how = ("the K steps as one hip graph, replayed once" if use_graph else
+           "the K steps launched eagerly, one launch each (K < %d)" % GRAPH_MIN_STEPS)
+    return (how + " (value, ms_per_step: host wall clock with a synchronize on both sides; "
+            "graph / eager: both ways' figures, event_us_per_step from HIP events around "
+            "them); roofline.kernel_avg_us: HIP events around a later replay of the graph "
+            "queued behind others, i.e. the launches' own GPU time back to back")
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -286,7 +300,9 @@ def bench_wgrad(args):
     esize = 2 if L.dtype == "bf16" else 4
     alg_bytes = (L.N * L.H * L.W * L.C + L.N * L.Ho * L.Wo * L.K) * esize + \
         L.R * L.S * L.C * L.K * 4
-    value = ops * args.steps / wall / 1e12
+    use_graph = args.steps >= GRAPH_MIN_STEPS
+    wall_timed = wall if use_graph else wall_eager
+    value = ops * args.steps / wall_timed / 1e12
     peak = PEAK_TOPS[L.dtype]
     achieved = ops / (step_ms * 1e-3) / 1e12
     kernels = plan.kernel_name + ("+wgrad_reduce" if plan.workspace_bytes else "")
@@ -297,7 +313,7 @@ def bench_wgrad(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "ms_per_step": round(wall_timed / args.steps * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -308,10 +324,14 @@ def bench_wgrad(args):
                    "padding": L.padding, "kernel": kernels,
                    "pixel_ranges": plan.workspace_bytes // (16 * ((L.R * L.S * L.C * L.K + 3)
                                                                  // 4)) or 1},
-        "launch": LAUNCH_NOTE,
+        "launch": launch_note(use_graph),
         "pct_of_mfma_peak": round(100.0 * value / peak, 3),
         "graph_event_us_per_step": round(graph_event_ms * 1e3, 3),
+        "graph": {"value": round(ops * args.steps / wall / 1e12, 4),
+                  "ms_per_step": round(wall / args.steps * 1e3, 6),
+                  "event_us_per_step": round(graph_event_ms * 1e3, 3)},
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
+                  "ms_per_step": round(wall_eager / args.steps * 1e3, 6),
                   "event_us_per_step": round(eager_ms * 1e3, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -515,7 +535,9 @@ def main():
     wall_full = time.perf_counter() - t2
 
     ops = L.ops_count()
-    value = ops * args.steps / wall / 1e12
+    use_graph = args.steps >= GRAPH_MIN_STEPS
+    wall_timed = wall if use_graph else wall_eager
+    value = ops * args.steps / wall_timed / 1e12
     alg_bytes = algorithmic_bytes(L, args.per_channel_scale)
     # The committed counters were taken with the default epilogue.
     traffic = (None if args.per_channel_scale or args.cudnn7_order or args.activation
@@ -537,7 +559,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "ms_per_step": round(wall_timed / args.steps * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -554,9 +576,12 @@ def main():
                      (order, "per-channel" if args.per_channel_scale else "scalar")
                      if L.dtype == "int8" else "bias, batch norm, " +
                      (args.activation or "relu")),
-        "launch": LAUNCH_NOTE,
+        "launch": launch_note(use_graph),
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TOPS[L.dtype], 3),
         "graph_event_us_per_step": round(graph_event_ms * 1e3, 3),
+        "graph": {"value": round(ops * args.steps / wall / 1e12, 4),
+                  "ms_per_step": round(wall / args.steps * 1e3, 6),
+                  "event_us_per_step": round(graph_event_ms * 1e3, 3)},
         "eager": {"value": round(ops * args.steps / wall_eager / 1e12, 4),
                   "ms_per_step": round(wall_eager / args.steps * 1e3, 6),
                   "event_us_per_step": round(eager_ms * 1e3, 3)},
