@@ -488,3 +488,63 @@ def test_tile_shapes_pinned_heights(C, K, H, W, R, stride, pad, dtype, bm, monke
     tol = TOL["fp32"] if R * R * C > 4096 else 2e-6
     name = check_case(tile_case(C, K, H, W, R, stride, pad, dtype), dtype, fp32_tol=tol)
     assert name.startswith("conv_tile_"), name
+
+
+@pytest.mark.parametrize("dtype,roles,seed", [("int8", "1", 410), ("int8", "0", 411),
+                                              ("bf16", "1", 420), ("bf16", "0", 421)])
+def test_fuzz_tiled_kernels(dtype, roles, seed, monkeypatch):
+    """Random layers on the tiled kernels (with copy waves, FCONV_TILE_ROLES=1,
+    and the 8-wave one): channels filling whole 128-byte stages, K any
+    multiple of 16, filters 1-5 in each direction, strides 1-3, SAME and
+    VALID, 64- and 128-pixel tiles, ragged pixel and channel tails."""
+    rng = np.random.default_rng(seed)
+    monkeypatch.setenv("FCONV_FORCE_VARIANT", "tile")
+    monkeypatch.setenv("FCONV_TILE_ROLES", roles)
+    count = 48
+    say("tiled fuzz %s roles=%s: %d cases" % (dtype, roles, count))
+    for i in range(count):
+        C = int(rng.choice([128, 256] if dtype == "int8" else [64, 128, 192]))
+        K = int(16 * rng.integers(1, 17))
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        st = int(rng.integers(1, 4))
+        pad = "SAME" if rng.random() < 0.6 else "VALID"
+        N = int(rng.integers(1, 4))
+        H = int(rng.integers(max(R, 3), 15))
+        W = int(rng.integers(max(S, 3), 15))
+        bm = str(rng.choice([64, 128]))
+        monkeypatch.setenv("FCONV_TILE_BM", bm)
+        Ho, Wo = oracle.geometry(H, W, R, S, st, st, pad == "SAME")[:2]
+        if dtype == "int8":
+            x = wl.draw_int8(rng, (N, H, W, C), -128, 127)
+            w = wl.draw_int8(rng, (R, S, C, K), -128, 127)
+            use_side = bool(rng.random() < 0.5)
+            relu = bool(rng.random() < 0.5)
+            c = dict(shape=(N, H, W, C, K, R, S, st, pad), x=x, w=w,
+                     bias=rng.normal(0, 30, K).astype(np.float32),
+                     side=wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if use_side else None,
+                     cis=np.float32(rng.choice([2.0 ** -10, 0.0123, 2.0 ** -13])),
+                     sis=np.float32(0.5) if use_side else np.float32(0), relu=relu,
+                     ops=[wl.OP_SCALE] + ([wl.OP_SIDE] if use_side else []) + [wl.OP_BIAS] +
+                     ([wl.OP_RELU] if relu else []), bn=None, use_bias=True)
+        else:
+            x = wl.float_to_bf16_bits(rng.normal(0, 1, (N, H, W, C)).astype(np.float32))
+            w = wl.float_to_bf16_bits(
+                rng.normal(0, 1 / np.sqrt(R * S * C), (R, S, C, K)).astype(np.float32))
+            use_bn = bool(rng.random() < 0.6)
+            relu = bool(rng.random() < 0.5)
+            bn = dict(mean=rng.normal(0, .1, K).astype(np.float32),
+                      var=rng.uniform(.5, 1.5, K).astype(np.float32),
+                      gamma=rng.uniform(.5, 1.5, K).astype(np.float32),
+                      beta=rng.normal(0, .1, K).astype(np.float32), eps=1e-5) if use_bn else None
+            c = dict(shape=(N, H, W, C, K, R, S, st, pad), x=x, w=w,
+                     bias=rng.normal(0, .1, K).astype(np.float32), side=None, cis=1.0, sis=0.0,
+                     relu=relu, ops=[wl.OP_BIAS] + ([wl.OP_BN] if use_bn else []) +
+                     ([wl.OP_RELU] if relu else []), bn=bn, use_bias=True)
+        y, r, guards, plan = _run_case(c, dtype)
+        where = "case %d %s bm=%s %s" % (i, c["shape"], bm, plan.kernel_name)
+        assert plan.kernel_name.startswith("conv_tile_"), where
+        assert guards, where
+        if dtype == "int8":
+            assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)
+        else:
+            assert float_error(y, r) <= TOL["bf16"], where
