@@ -548,3 +548,48 @@ def test_fuzz_tiled_kernels(dtype, roles, seed, monkeypatch):
             assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)
         else:
             assert float_error(y, r) <= TOL["bf16"], where
+
+
+def test_fuzz_halo_s2():
+    """Random layers on the stride-2 row kernel: 64 or 128 input channels, K a
+    multiple of 128, Wo up to 31, SAME (either stride-2 padding) and VALID,
+    images of one output row and up, ragged last workgroups, rows per
+    workgroup from the device size or pinned (FCONV_HALO_ROWS), with and
+    without the side input and ReLU; bit-exact against the oracle."""
+    import os
+    rng = np.random.default_rng(430)
+    count = 20
+    say("halo_s2 fuzz: %d cases" % count)
+    for i in range(count):
+        C = int(rng.choice([64, 128]))
+        K = int(128 * rng.integers(1, 3))
+        N = int(rng.integers(1, 4))
+        pad = "SAME" if rng.random() < 0.7 else "VALID"
+        H = int(rng.integers(3, 40))
+        W = int(rng.integers(3, 62))
+        Ho, Wo = oracle.geometry(H, W, 3, 3, 2, 2, pad == "SAME")[:2]
+        rows = int(rng.choice([0, 1, 2, 3, 5, 9]))
+        if rows:
+            os.environ["FCONV_HALO_ROWS"] = str(rows)
+        else:
+            os.environ.pop("FCONV_HALO_ROWS", None)
+        try:
+            side = bool(rng.random() < 0.5)
+            relu = bool(rng.random() < 0.5)
+            x = wl.draw_int8(rng, (N, H, W, C), -128, 127)
+            w = wl.draw_int8(rng, (3, 3, C, K), -128, 127)
+            c = dict(shape=(N, H, W, C, K, 3, 3, 2, pad), x=x, w=w,
+                     bias=rng.normal(0, 40, K).astype(np.float32),
+                     side=wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if side else None,
+                     cis=np.float32(rng.choice([2.0 ** -11, 2.0 ** -12, 0.0009])),
+                     sis=np.float32(0.75 if side else 0.0), relu=relu,
+                     ops=[wl.OP_SCALE] + ([wl.OP_SIDE] if side else []) + [wl.OP_BIAS] +
+                     ([wl.OP_RELU] if relu else []), bn=None, use_bias=True)
+            y, r, guards, plan = _run_case(c, "int8")
+        finally:
+            os.environ.pop("FCONV_HALO_ROWS", None)
+        where = "case %d %s rows=%d %s" % (i, c["shape"], rows, plan.kernel_name)
+        if Wo <= 31:
+            assert plan.kernel_name == "conv_halo_s2_i8", where
+        assert guards, where
+        assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)

@@ -226,3 +226,34 @@ def test_wgrad_layer_shapes(shape, dtype):
     e = float_error(got, ref)
     say("  normwise error", e)
     assert e <= TOL["fp32"], (shape, dtype, e)
+
+
+@pytest.mark.parametrize("pin", ["default", "halo"])
+def test_wgrad_fuzz_row_halo(pin, monkeypatch):
+    """Random bf16 3x3 stride-1 layers on the row-halo weight-gradient kernel:
+    32-channel input slices (C = 32, 64, 96), 64-channel output blocks,
+    padded rows of up to 64 pixels (one-row steps past 32 output columns;
+    pinned, FCONV_WGRAD_KERNEL=halo, two-row steps on narrower rows), SAME
+    and VALID, images of one output row and up, ranges that cross images."""
+    _pin(pin, monkeypatch)
+    rng = np.random.default_rng(440 if pin == "default" else 441)
+    dev = device()
+    count = 16
+    say("row-halo wgrad fuzz (%s): %d cases" % (pin, count))
+    for i in range(count):
+        C = int(rng.choice([32, 64, 96]))
+        K = int(rng.choice([64, 128]))
+        N = int(rng.integers(1, 4))
+        pad = "SAME" if rng.random() < 0.7 else "VALID"
+        H = int(rng.integers(3, 12))
+        W = int(rng.integers(35, 63)) if pin == "default" else int(rng.integers(3, 63))
+        plan = fc.WgradPlan(N, H, W, C, K, 3, 3, 1, pad, "bf16", out_fp32=True)
+        where = (i, (N, H, W, C, K, pad), plan.kernel_name)
+        if pin == "default":
+            assert plan.kernel_name == "wgrad_halo_bf16", where
+        x = draw(rng, (N, H, W, C), "bf16")
+        dy = draw(rng, plan.dy_shape, "bf16")
+        got = run_wgrad(plan, x, dy, dev, fill=7.0)
+        ref = oracle.wgrad(x, dy, 3, 3, 1, pad)
+        e = float_error(got, ref)
+        assert e <= TOL[plan.out_dtype], (where, e)
