@@ -593,3 +593,49 @@ def test_fuzz_halo_s2():
             assert plan.kernel_name == "conv_halo_s2_i8", where
         assert guards, where
         assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)
+
+
+@pytest.mark.parametrize("cudnn7", [False, True])
+def test_fuzz_halo(cudnn7):
+    """Random layers on the stride-1 row kernel (the benchmark layer's
+    kernel): 3x3 over 64 channels, K any multiple of 16, padded rows of up to
+    64 pixels, SAME and VALID, images of one row and up, workgroups spanning
+    images, rows per workgroup from the device size or pinned
+    (FCONV_HALO_ROWS), with and without the side input and ReLU, in both
+    epilogue orders; bit-exact against the oracle."""
+    import os
+    rng = np.random.default_rng(450 + int(cudnn7))
+    count = 24
+    say("halo fuzz (cudnn7 order %s): %d cases" % (cudnn7, count))
+    for i in range(count):
+        K = int(16 * rng.integers(1, 9))
+        N = int(rng.integers(1, 12))
+        pad = "SAME" if rng.random() < 0.7 else "VALID"
+        H = int(rng.integers(1 if pad == "SAME" else 3, 13))
+        W = int(rng.integers(1 if pad == "SAME" else 3, 63))
+        rows = int(rng.choice([0, 0, 1, 2, 4, 7, 11]))
+        side = bool(rng.random() < 0.6)
+        relu = bool(rng.random() < 0.5)
+        Ho, Wo = oracle.geometry(H, W, 3, 3, 1, 1, pad == "SAME")[:2]
+        x = wl.draw_int8(rng, (N, H, W, 64), -128, 127)
+        w = wl.draw_int8(rng, (3, 3, 64, K), -128, 127)
+        bias = rng.normal(0, 40, K).astype(np.float32)
+        sd = wl.draw_int8(rng, (N, Ho, Wo, K), -128, 127) if side else None
+        cis = np.float32(rng.choice([2.0 ** -11, 2.0 ** -9, 0.0007]))
+        sis = np.float32(0.25 if side else 0.0)
+        ops = [wl.OP_SCALE] + ([wl.OP_SIDE] if side else []) + [wl.OP_BIAS] + (
+            [wl.OP_RELU] if relu else [])
+        if rows:
+            os.environ["FCONV_HALO_ROWS"] = str(rows)
+        try:
+            plan = make_plan(N, H, W, 64, K, 3, 3, 1, pad, "int8", ops, cudnn7_order=cudnn7)
+        finally:
+            os.environ.pop("FCONV_HALO_ROWS", None)
+        where = "case %d %s rows=%d %s" % (i, (N, H, W, K, pad, side, relu), rows,
+                                           plan.kernel_name)
+        assert plan.kernel_name == "conv_halo_i8", where
+        y, guards = run_gpu(plan, "int8", x, w, bias, sd, cis, sis, guard=64)
+        r = oracle_out("int8", x, w, 1, pad, bias, sd, cis, sis, relu,
+                       order=7 if cudnn7 else 8)
+        assert guards, where
+        assert np.array_equal(y, r), where + ": %d differ" % np.count_nonzero(y != r)
